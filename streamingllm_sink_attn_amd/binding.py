@@ -1,0 +1,249 @@
+"""Thin Python binding over libsinkattn.so (ctypes).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory (outputs and workspace) and the current stream.
+If the library is not built the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsinkattn.so")
+
+BF16, F32 = 0, 1
+OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
+BLOCK_SIZE = 64
+
+c_i32 = ctypes.c_int32
+c_vp = ctypes.c_void_p
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [
+        ("cu_seqlens", c_vp),
+        ("batch", c_i32),
+        ("total_tokens", c_i32),
+        ("max_seqlen", c_i32),
+        ("num_q_heads", c_i32),
+        ("num_kv_heads", c_i32),
+        ("head_dim", c_i32),
+        ("dtype", c_i32),
+        ("softmax_scale", ctypes.c_float),
+        ("n_sink", c_i32),
+        ("window", c_i32),
+        ("block_indices", c_vp),
+        ("num_q_blocks", c_i32),
+        ("block_size", c_i32),
+        ("max_blocks", c_i32),
+        ("learnable_sink", c_vp),
+    ]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("cache_seqlens", c_vp),
+        ("batch", c_i32),
+        ("slots", c_i32),
+        ("num_q_heads", c_i32),
+        ("num_kv_heads", c_i32),
+        ("head_dim", c_i32),
+        ("dtype", c_i32),
+        ("softmax_scale", ctypes.c_float),
+        ("learnable_sink", c_vp),
+        ("num_splits", c_i32),
+    ]
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sink_attn status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_SIGS = {
+    "sink_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                              c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_fwd_workspace_size": (ctypes.c_size_t, [c_vp]),
+    "sink_attn_bwd_workspace_size": (ctypes.c_size_t, [c_vp]),
+    "sink_attn_decode_workspace_size": (ctypes.c_size_t, [c_vp]),
+    "sink_attn_check_fwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t]),
+    "sink_attn_check_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    ctypes.c_size_t]),
+    "sink_attn_check_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t]),
+    "sink_attn_strerror": (ctypes.c_char_p, [c_i32]),
+    "sink_attn_last_error": (ctypes.c_char_p, []),
+    "sink_attn_prefill_path": (c_i32, [c_vp]),
+    "sink_attn_debug_visit_map": (c_i32, [c_vp, c_vp, ctypes.c_size_t, c_vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m streamingllm_sink_attn_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        detail = lib().sink_attn_last_error().decode()
+        raise SinkAttnError(status, f"{lib().sink_attn_strerror(status).decode()}: {detail}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else c_vp(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise SinkAttnError(UNSUPPORTED, f"dtype {t.dtype} not supported")
+
+
+def _stream(stream) -> c_vp:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_vp(stream.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise SinkAttnError(INVALID_ARGUMENT, "tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise SinkAttnError(INVALID_ARGUMENT, "tensors must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prefill_desc(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                 softmax_scale: float, n_sink: int = 0, window: int = 0,
+                 block_indices: Optional[torch.Tensor] = None,
+                 learnable_sink: Optional[torch.Tensor] = None) -> PrefillDesc:
+    T, hq, d = q.shape
+    nqb = int(block_indices.shape[0]) if block_indices is not None else 0
+    kb = int(block_indices.shape[2]) if block_indices is not None else 0
+    return PrefillDesc(
+        cu_seqlens=cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+        batch=(cu_seqlens.numel() - 1) if cu_seqlens is not None else 0,
+        total_tokens=T, max_seqlen=int(max_seqlen), num_q_heads=hq, num_kv_heads=int(k.shape[1]),
+        head_dim=d, dtype=_dtype_code(q), softmax_scale=float(softmax_scale), n_sink=int(n_sink),
+        window=int(window),
+        block_indices=block_indices.data_ptr() if block_indices is not None else None,
+        num_q_blocks=nqb, block_size=BLOCK_SIZE, max_blocks=kb,
+        learnable_sink=learnable_sink.data_ptr() if learnable_sink is not None else None)
+
+
+def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: Optional[int]) -> int:
+    if max_seqlen is not None:
+        return int(max_seqlen)
+    c = cu_seqlens.detach().to("cpu")
+    return int((c[1:] - c[:-1]).max().item()) if c.numel() > 1 else 0
+
+
+def fwd(q, k, v, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,
+        block_indices=None, learnable_sink=None, return_s=True, out=None, stream=None):
+    """Forward.  Returns (o [T,Hq,D], lse [T,Hq] float32 L_orig, s [T,Hq] or None)."""
+    _need_cuda(q, k, v, cu_seqlens, block_indices, learnable_sink)
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    desc = prefill_desc(q, k, cu_seqlens, _max_seqlen(cu_seqlens, max_seqlen), scale, n_sink, window,
+                        block_indices, learnable_sink)
+    T, hq, _ = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+    s = torch.empty((T, hq), dtype=torch.float32, device=q.device) if return_s else None
+    L = lib()
+    ws_bytes = L.sink_attn_fwd_workspace_size(ctypes.byref(desc))
+    ws = _workspace(ws_bytes, q.device)
+    _check(L.sink_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
+                           _p(ws), ws_bytes, _stream(stream)))
+    return o, lse, s
+
+
+def bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,
+        block_indices=None, learnable_sink=None, stream=None):
+    """Backward.  Returns (dq, dk, dv, dsink float32 [Hq] or None)."""
+    _need_cuda(q, k, v, o, lse, dout, cu_seqlens, block_indices, learnable_sink)
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    desc = prefill_desc(q, k, cu_seqlens, _max_seqlen(cu_seqlens, max_seqlen), scale, n_sink, window,
+                        block_indices, learnable_sink)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsink = (torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
+             if learnable_sink is not None else None)
+    L = lib()
+    ws_bytes = L.sink_attn_bwd_workspace_size(ctypes.byref(desc))
+    ws = _workspace(ws_bytes, q.device)
+    _check(L.sink_attn_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout),
+                           _p(dq), _p(dk), _p(dv), _p(dsink), _p(ws), ws_bytes, _stream(stream)))
+    return dq, dk, dv, dsink
+
+
+def decode_desc(q, k_cache, softmax_scale, cache_seqlens=None, learnable_sink=None,
+                num_splits=0) -> DecodeDesc:
+    B, hq, d = q.shape
+    return DecodeDesc(
+        cache_seqlens=cache_seqlens.data_ptr() if cache_seqlens is not None else None,
+        batch=B, slots=int(k_cache.shape[1]), num_q_heads=hq, num_kv_heads=int(k_cache.shape[2]),
+        head_dim=d, dtype=_dtype_code(q), softmax_scale=float(softmax_scale),
+        learnable_sink=learnable_sink.data_ptr() if learnable_sink is not None else None,
+        num_splits=int(num_splits))
+
+
+def decode(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, learnable_sink=None,
+           num_splits=0, return_s=True, out=None, stream=None):
+    """Decode.  Returns (o [B,Hq,D], lse [B,Hq] L_orig, s [B,Hq] or None)."""
+    _need_cuda(q, k_cache, v_cache, cache_seqlens, learnable_sink)
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    desc = decode_desc(q, k_cache, scale, cache_seqlens, learnable_sink, num_splits)
+    B, hq, _ = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
+    L = lib()
+    ws_bytes = L.sink_attn_decode_workspace_size(ctypes.byref(desc))
+    ws = _workspace(ws_bytes, q.device)
+    _check(L.sink_attn_decode(ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(o), _p(lse),
+                              _p(s), _p(ws), ws_bytes, _stream(stream)))
+    return o, lse, s
+
+
+def prefill_path(q, k, cu_seqlens, max_seqlen, n_sink=0, window=0, block_indices=None) -> int:
+    desc = prefill_desc(q, k, cu_seqlens, max_seqlen, 1.0, n_sink, window, block_indices, None)
+    return int(lib().sink_attn_prefill_path(ctypes.byref(desc)))
+
+
+def debug_visit_map(q, k, cu_seqlens, max_seqlen, n_sink=0, window=0, block_indices=None,
+                    stream=None) -> torch.Tensor:
+    """uint8 [Hkv * max_seqlen * T] buffer; sample b's masks start at
+    Hkv * sum_{b'<b} L_b'^2, each [L_b, L_b] row-major per KV head."""
+    desc = prefill_desc(q, k, cu_seqlens, max_seqlen, 1.0, n_sink, window, block_indices, None)
+    nbytes = int(k.shape[1]) * int(max_seqlen) * int(q.shape[0])
+    out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().sink_attn_debug_visit_map(ctypes.byref(desc), _p(out), nbytes, _stream(stream)))
+    return out

@@ -1,0 +1,273 @@
+// Backward pieces shared by the generic and MFMA paths:
+//   * preprocess: Delta = rowsum(dO * O_new), L_new = log(e^{L_orig} + e^{a_h}),
+//     p_sink = e^{a_h - L_new} and the per-row sink-gradient term
+//     -Delta * p_sink ("Attention Sink, Learnable Sink and dsink" s7 boxed
+//     equation; s10 prefers e^{sink - lse_total} over 1 - s near s = 1);
+//   * the reverse block lists (per KV block: the query blocks selecting it),
+//     so that a KV-major backward visits each (KV block, query block) pair
+//     once and never adds the sink term per visit (s10);
+//   * finish: dsink as a fixed-order sum of the per-row terms (deterministic),
+//     and float32 accumulators converted to the output dtype.
+#include "common.cuh"
+
+namespace sa {
+
+// 16 lanes per (token, head) row, 16-byte chunks.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(Prefill p, const void* __restrict__ o,
+                                                             const float* __restrict__ lse,
+                                                             const void* __restrict__ dout,
+                                                             BwdWork w, int zero_dq) {
+  constexpr int kPerChunk = 16 / sizeof(T);
+  const int D = p.d;
+  const int nchunks = D / kPerChunk;
+  const size_t R = static_cast<size_t>(p.total) * p.hq;
+  const int sub = threadIdx.x & 15;
+  const size_t rows_per_step = static_cast<size_t>(gridDim.x) * (blockDim.x / 16);
+  for (size_t row = static_cast<size_t>(blockIdx.x) * (blockDim.x / 16) + threadIdx.x / 16; row < R;
+       row += rows_per_step) {
+    float acc = 0.f;
+    for (int c = sub; c < nchunks; c += 16) {
+      const size_t off = row * D + static_cast<size_t>(c) * kPerChunk;
+      u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const T*>(o) + off);
+      u32x4 dv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(dout) + off);
+      if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += __uint_as_float(ov[e]) * __uint_as_float(dv[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc += __uint_as_float(ov[e] << 16) * __uint_as_float(dv[e] << 16);
+          acc += __uint_as_float(ov[e] & 0xffff0000u) * __uint_as_float(dv[e] & 0xffff0000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (zero_dq) {
+      for (int e = sub * 4; e < D; e += 64)
+        *reinterpret_cast<f32x4*>(w.dq_acc + row * D + e) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (sub == 0) {
+      const int h = static_cast<int>(row % p.hq);
+      const float L = lse[row];
+      float lnew, ps;
+      if (p.sink != nullptr) {
+        const float a = p.sink[h];
+        if (L == -kInf) {
+          lnew = a;
+        } else {
+          const float mx = fmaxf(L, a);
+          lnew = mx + log1pf(expf(-fabsf(L - a)));
+        }
+        ps = expf(a - lnew);
+      } else {
+        lnew = (L == -kInf) ? kInf : L;   // +inf makes every recomputed P exactly 0
+        ps = 0.f;
+      }
+      w.delta[row] = acc;
+      w.lnew[row] = lnew;
+      w.dsink_terms[row] = -acc * ps;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ ptr, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x * 4;
+  for (size_t i = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<f32x4*>(ptr + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      for (size_t e = i; e < n; ++e) ptr[e] = 0.f;
+    }
+  }
+}
+
+static int grid_for(size_t work, int per_block) {
+  size_t g = (work + per_block - 1) / per_block;
+  if (g > 8192) g = 8192;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+__global__ __launch_bounds__(256) void fill_zero_bytes_kernel(uint8_t* __restrict__ ptr, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    ptr[i] = 0;
+}
+
+hipError_t launch_fill_zero(float* ptr, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 1024)), dim3(256), 0, st, ptr, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_bytes(uint8_t* ptr, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_bytes_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, ptr, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* lse,
+                                 const void* dout, const BwdWork& w, bool zero_dq,
+                                 bool zero_dkv, hipStream_t st) {
+  if (p.total == 0) return hipSuccess;
+  const size_t R = static_cast<size_t>(p.total) * p.hq;
+  const int grid = grid_for(R, 16);
+  if (p.dtype == SINK_ATTN_F32)
+    hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(256), 0, st, p, o, lse, dout,
+                       w, zero_dq ? 1 : 0);
+  else
+    hipLaunchKernelGGL(bwd_preprocess_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p, o, lse,
+                       dout, w, zero_dq ? 1 : 0);
+  if (zero_dkv) {
+    const size_t n = static_cast<size_t>(p.total) * p.hkv * p.d;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 1024)), dim3(256), 0, st, w.dk_acc, n);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 1024)), dim3(256), 0, st, w.dv_acc, n);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Reverse block lists.  For global KV block kbg (= sample offset + local kb)
+// and KV head g: the sample-local query blocks qb >= kb whose row selects kb,
+// in increasing qb order (so the fill is deterministic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void locate_block(const int32_t* cu, int batch, int kbg, int* b_out,
+                                             int* off_out) {
+  int off = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int n = (cu[b + 1] - cu[b] + kBlock - 1) / kBlock;
+    if (kbg < off + n) { *b_out = b; *off_out = off; return; }
+    off += n;
+  }
+  *b_out = batch - 1; *off_out = off;
+}
+
+template <bool kFill>
+__global__ __launch_bounds__(256) void block_csr_kernel(Prefill p, BwdWork w) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= p.nqb * p.hkv) return;
+  const int kbg = idx / p.hkv;
+  const int g = idx % p.hkv;
+  int b, off;
+  locate_block(p.cu, p.batch, kbg, &b, &off);
+  const int kb = kbg - off;
+  const int nqb_b = (p.cu[b + 1] - p.cu[b] + kBlock - 1) / kBlock;
+  int n = 0;
+  int32_t* dst = kFill ? w.csr_idx + w.csr_off[idx] : nullptr;
+  for (int qb = kb; qb < nqb_b; ++qb) {
+    const int32_t* row = p.blocks + (static_cast<size_t>(off + qb) * p.hkv + g) * p.max_blocks;
+    if (row_selects(row, p.max_blocks, kb)) {
+      if (kFill) dst[n] = qb;
+      ++n;
+    }
+  }
+  if (!kFill) w.csr_off[idx + 1] = n;
+}
+
+// Exclusive scan of csr_off[1..n] in place (csr_off[0] = 0), one workgroup.
+__global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* off, int n) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int a = tid * per, e = min(n, a + per);
+  int32_t sum = 0;
+  for (int i = a; i < e; ++i) sum += off[i + 1];
+  part[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    int32_t v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid ? part[tid - 1] : 0;
+  for (int i = a; i < e; ++i) {
+    const int32_t c = off[i + 1];
+    off[i + 1] = run + c;
+    run += c;
+  }
+  if (tid == 0) off[0] = 0;
+}
+
+hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st) {
+  const int n = p.nqb * p.hkv;
+  if (n == 0) return hipSuccess;
+  const int grid = (n + 255) / 256;
+  hipLaunchKernelGGL(block_csr_kernel<false>, dim3(grid), dim3(256), 0, st, p, w);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, st, w.csr_off, n);
+  hipLaunchKernelGGL(block_csr_kernel<true>, dim3(grid), dim3(256), 0, st, p, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Finish: dsink[h] = sum_t terms[t, h] in a fixed order; accumulators -> dtype.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dsink_reduce_kernel(const float* __restrict__ terms, int T,
+                                                           int hq, float* __restrict__ dsink) {
+  __shared__ float red[256];
+  const int h = blockIdx.x;
+  float acc = 0.f;
+  for (int t = threadIdx.x; t < T; t += 256) acc += terms[static_cast<size_t>(t) * hq + h];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsink[h] = red[0];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, void* dst,
+                                                      size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x * 4;
+  for (size_t i = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
+      if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + i) = x;
+      } else {
+        uint16_t* d = static_cast<uint16_t*>(dst) + i;
+        u32x2 packed;
+        packed[0] = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+        packed[1] = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+        *reinterpret_cast<u32x2*>(d) = packed;
+      }
+    } else {
+      for (size_t e = i; e < n; ++e) Elem<T>::store(dst, e, src[e]);
+    }
+  }
+}
+
+template <typename T>
+static void convert(const float* src, void* dst, size_t n, hipStream_t st) {
+  if (n == 0) return;
+  hipLaunchKernelGGL(convert_kernel<T>, dim3(grid_for(n, 1024)), dim3(256), 0, st, src, dst, n);
+}
+
+hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq, void* dk,
+                             void* dv, bool dq_from_acc, bool dkv_from_acc, hipStream_t st) {
+  if (dsink != nullptr)
+    hipLaunchKernelGGL(dsink_reduce_kernel, dim3(p.hq), dim3(256), 0, st, w.dsink_terms, p.total,
+                       p.hq, dsink);
+  const size_t nq = static_cast<size_t>(p.total) * p.hq * p.d;
+  const size_t nkv = static_cast<size_t>(p.total) * p.hkv * p.d;
+  const bool f32 = p.dtype == SINK_ATTN_F32;
+  if (dq_from_acc) {
+    if (f32) convert<float>(w.dq_acc, dq, nq, st); else convert<uint16_t>(w.dq_acc, dq, nq, st);
+  }
+  if (dkv_from_acc) {
+    if (f32) {
+      convert<float>(w.dk_acc, dk, nkv, st);
+      convert<float>(w.dv_acc, dv, nkv, st);
+    } else {
+      convert<uint16_t>(w.dk_acc, dk, nkv, st);
+      convert<uint16_t>(w.dv_acc, dv, nkv, st);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,78 @@
+// Internal declarations shared by the C-ABI layer and the kernel sources.
+// Host-visible structs hold only plain pointers and sizes; kernels take them
+// by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sink_attn.h"
+
+namespace sa {
+
+// Everything a prefill kernel needs to know about the problem.
+struct Prefill {
+  const int32_t* cu;          // [batch+1]
+  int batch, total, max_seqlen;
+  int hq, hkv, d, dtype;
+  float scale;
+  int n_sink, window;         // window <= 0: no window (n_sink ignored)
+  const int32_t* blocks;      // [nqb, hkv, max_blocks] or nullptr
+  int nqb, max_blocks;
+  const float* sink;          // [hq] or nullptr
+};
+
+// Backward workspace carve-up (float32 unless noted).
+struct BwdWork {
+  float* delta;      // [T, Hq]  rowsum(dO * O)
+  float* lnew;       // [T, Hq]  log(Z + e^a) (or L_orig; +inf for empty rows without a sink)
+  float* dsink_terms;// [T, Hq]  -Delta * p_sink per row
+  float* dq_acc;     // [T, Hq, D]  (MFMA path) accumulated dQ
+  float* dk_acc;     // [T, Hkv, D] (generic path, and the MFMA path's split sink tiles)
+  float* dv_acc;     // [T, Hkv, D]
+  int32_t* csr_off;  // [nqb*Hkv + 1]  (block mode) per (KV block, KV head) list offsets
+  int32_t* csr_idx;  // [nqb*Hkv*max_blocks] query blocks selecting each KV block
+};
+
+struct Decode {
+  const int32_t* cache_seqlens;
+  int batch, slots, hq, hkv, d, dtype;
+  float scale;
+  const float* sink;
+  int splits;
+};
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----
+hipError_t launch_fwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
+                              void* o, float* lse, float* s, hipStream_t st);
+hipError_t launch_fwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
+                           void* o, float* lse, float* s, hipStream_t st);
+bool fwd_mfma_supported(const Prefill& p);
+
+hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* lse,
+                                 const void* dout, const BwdWork& w, bool zero_dq,
+                                 bool zero_dkv, hipStream_t st);
+hipError_t launch_bwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
+                              const void* dout, const BwdWork& w, void* dq, hipStream_t st);
+hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
+                           const void* dout, const BwdWork& w, void* dk, void* dv,
+                           hipStream_t st);
+bool bwd_mfma_supported(const Prefill& p);
+hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st);
+hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq,
+                             void* dk, void* dv, bool dq_from_acc, bool dkv_from_acc,
+                             hipStream_t st);
+
+hipError_t launch_decode(const Decode& p, const void* q, const void* kc, const void* vc,
+                         void* o, float* lse, float* s, float* ws, hipStream_t st);
+int decode_auto_splits(const Decode& p);
+bool decode_mfma_supported(const Decode& p);
+
+hipError_t launch_visit_map(const Prefill& p, uint8_t* out, hipStream_t st);
+
+// Fill kernels (used instead of hipMemsetAsync so callers may capture graphs).
+hipError_t launch_fill_zero(float* ptr, size_t n, hipStream_t st);
+hipError_t launch_fill_zero_bytes(uint8_t* ptr, size_t n, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,386 @@
+// C-ABI entry points: host-side validation, workspace carve-up and dispatch
+// to the kernels.  Nothing here reads device memory, allocates, frees or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Longest sample allowed with block lists (the forward's block bitmap).
+constexpr int kMaxBlockSeqlen = 8192 * SINK_ATTN_BLOCK_SIZE;
+
+int check_prefill_desc(const sink_attn_prefill_desc* d) {
+  if (d == nullptr) return fail(SINK_ATTN_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "batch < 0");
+  if (d->batch > 0 && d->cu_seqlens == nullptr)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  if (d->total_tokens < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "total_tokens < 0");
+  if (d->max_seqlen < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "max_seqlen < 0");
+  if (d->total_tokens > 0 && d->max_seqlen < 1)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "max_seqlen must be >= 1 when total_tokens > 0");
+  if (d->total_tokens > 0 && d->batch == 0)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "total_tokens > 0 with batch == 0");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "num_q_heads %% num_kv_heads != 0");
+  if (d->num_q_heads > 65535) return fail(SINK_ATTN_UNSUPPORTED, "num_q_heads > 65535");
+  if (d->dtype != SINK_ATTN_BF16 && d->dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->head_dim < 8 || d->head_dim > SINK_ATTN_MAX_HEAD_DIM || d->head_dim % 8 != 0)
+    return fail(SINK_ATTN_UNSUPPORTED, "head_dim %d not supported (multiple of 8, 8..%d)",
+                d->head_dim, SINK_ATTN_MAX_HEAD_DIM);
+  if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (d->n_sink < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "n_sink < 0");
+  if (d->block_indices != nullptr) {
+    if (d->block_size != SINK_ATTN_BLOCK_SIZE)
+      return fail(SINK_ATTN_UNSUPPORTED, "block_size %d not supported (must be %d)", d->block_size,
+                  SINK_ATTN_BLOCK_SIZE);
+    if (d->max_blocks < 1) return fail(SINK_ATTN_INVALID_ARGUMENT, "max_blocks < 1");
+    if (d->num_q_blocks < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "num_q_blocks < 0");
+    const long long need_min = (static_cast<long long>(d->total_tokens) + SINK_ATTN_BLOCK_SIZE - 1) /
+                               SINK_ATTN_BLOCK_SIZE;
+    if (d->num_q_blocks < need_min)
+      return fail(SINK_ATTN_INVALID_ARGUMENT, "num_q_blocks %d < ceil(total_tokens / %d)",
+                  d->num_q_blocks, SINK_ATTN_BLOCK_SIZE);
+    if (d->max_seqlen > kMaxBlockSeqlen)
+      return fail(SINK_ATTN_UNSUPPORTED, "max_seqlen > %d with block_indices", kMaxBlockSeqlen);
+  }
+  return SINK_ATTN_OK;
+}
+
+sa::Prefill to_prefill(const sink_attn_prefill_desc* d) {
+  sa::Prefill p;
+  p.cu = d->cu_seqlens;
+  p.batch = d->batch;
+  p.total = d->total_tokens;
+  p.max_seqlen = d->max_seqlen;
+  p.hq = d->num_q_heads;
+  p.hkv = d->num_kv_heads;
+  p.d = d->head_dim;
+  p.dtype = d->dtype;
+  p.scale = d->softmax_scale;
+  p.n_sink = d->n_sink;
+  p.window = d->window;
+  p.blocks = d->block_indices;
+  p.nqb = d->block_indices ? d->num_q_blocks : 0;
+  p.max_blocks = d->block_indices ? d->max_blocks : 0;
+  p.sink = d->learnable_sink;
+  return p;
+}
+
+size_t elem_size(int dtype) { return dtype == SINK_ATTN_F32 ? 4 : 2; }
+
+// Backward workspace layout (each section 256-byte aligned).
+struct BwdLayout {
+  size_t delta, lnew, terms, dq_acc, dk_acc, dv_acc, csr_off, csr_idx, total;
+};
+
+BwdLayout bwd_layout(const sa::Prefill& p) {
+  BwdLayout l{};
+  const size_t rows = static_cast<size_t>(p.total) * p.hq;
+  const size_t kv = static_cast<size_t>(p.total) * p.hkv * p.d;
+  const bool mfma = sa::bwd_mfma_supported(p);
+  size_t off = 0;
+  l.delta = off; off += round_up(rows * 4);
+  l.lnew = off; off += round_up(rows * 4);
+  l.terms = off; off += round_up(rows * 4);
+  l.dq_acc = off; off += mfma ? round_up(rows * p.d * 4) : 0;
+  l.dk_acc = off; off += round_up(kv * 4);
+  l.dv_acc = off; off += round_up(kv * 4);
+  const size_t nl = p.blocks ? static_cast<size_t>(p.nqb) * p.hkv : 0;
+  l.csr_off = off; off += (p.blocks && mfma) ? round_up((nl + 1) * 4) : 0;
+  l.csr_idx = off; off += (p.blocks && mfma) ? round_up(nl * p.max_blocks * 4) : 0;
+  l.total = off;
+  return l;
+}
+
+int check_decode_desc(const sink_attn_decode_desc* d) {
+  if (d == nullptr) return fail(SINK_ATTN_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "batch < 0");
+  if (d->batch > 0 && d->slots < 1) return fail(SINK_ATTN_INVALID_ARGUMENT, "slots < 1");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "num_q_heads %% num_kv_heads != 0");
+  if (d->num_q_heads > 65535) return fail(SINK_ATTN_UNSUPPORTED, "num_q_heads > 65535");
+  if (d->dtype != SINK_ATTN_BF16 && d->dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->head_dim < 8 || d->head_dim > SINK_ATTN_MAX_HEAD_DIM || d->head_dim % 8 != 0)
+    return fail(SINK_ATTN_UNSUPPORTED, "head_dim %d not supported", d->head_dim);
+  if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (d->num_splits < 0 || d->num_splits > 256)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "num_splits must be in [0, 256]");
+  return SINK_ATTN_OK;
+}
+
+sa::Decode to_decode(const sink_attn_decode_desc* d) {
+  sa::Decode p;
+  p.cache_seqlens = d->cache_seqlens;
+  p.batch = d->batch;
+  p.slots = d->slots;
+  p.hq = d->num_q_heads;
+  p.hkv = d->num_kv_heads;
+  p.d = d->head_dim;
+  p.dtype = d->dtype;
+  p.scale = d->softmax_scale;
+  p.sink = d->learnable_sink;
+  p.splits = d->num_splits;
+  if (p.splits == 0) p.splits = sa::decode_auto_splits(p);
+  if (p.splits > p.slots && p.slots > 0) p.splits = p.slots;
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+size_t decode_ws_bytes(const sa::Decode& p) {
+  if (!sa::decode_mfma_supported(p)) return 0;
+  // per (sequence, query head, split): acc[D] + (m, l)
+  return round_up(static_cast<size_t>(p.batch) * p.hq * p.splits * (p.d + 2) * 4);
+}
+
+int check_ptr(const void* ptr, const char* name, size_t align, bool required) {
+  if (ptr == nullptr) {
+    if (required) return fail(SINK_ATTN_INVALID_ARGUMENT, "%s is NULL", name);
+    return SINK_ATTN_OK;
+  }
+  if (!aligned(ptr, align))
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "%s is not %zu-byte aligned", name, align);
+  return SINK_ATTN_OK;
+}
+
+#define SA_TRY(expr)                 \
+  do {                               \
+    int _st = (expr);                \
+    if (_st != SINK_ATTN_OK) return _st; \
+  } while (0)
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SINK_ATTN_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+  return SINK_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sink_attn_strerror(int status) {
+  switch (status) {
+    case SINK_ATTN_OK: return "ok";
+    case SINK_ATTN_INVALID_ARGUMENT: return "invalid argument";
+    case SINK_ATTN_UNSUPPORTED: return "unsupported configuration";
+    case SINK_ATTN_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SINK_ATTN_HIP_ERROR: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* sink_attn_last_error(void) { return g_last_error; }
+
+size_t sink_attn_fwd_workspace_size(const sink_attn_prefill_desc* desc) {
+  (void)desc;
+  return 0;
+}
+
+size_t sink_attn_bwd_workspace_size(const sink_attn_prefill_desc* desc) {
+  if (check_prefill_desc(desc) != SINK_ATTN_OK) return 0;
+  return bwd_layout(to_prefill(desc)).total;
+}
+
+size_t sink_attn_decode_workspace_size(const sink_attn_decode_desc* desc) {
+  if (check_decode_desc(desc) != SINK_ATTN_OK) return 0;
+  return decode_ws_bytes(to_decode(desc));
+}
+
+int sink_attn_prefill_path(const sink_attn_prefill_desc* desc) {
+  if (check_prefill_desc(desc) != SINK_ATTN_OK) return -1;
+  return sa::fwd_mfma_supported(to_prefill(desc)) ? 1 : 0;
+}
+
+int sink_attn_check_fwd(const sink_attn_prefill_desc* desc, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const float* s,
+                        size_t workspace_bytes) {
+  SA_TRY(check_prefill_desc(desc));
+  const bool need = desc->total_tokens > 0;
+  SA_TRY(check_ptr(q, "q", 16, need));
+  SA_TRY(check_ptr(k, "k", 16, need));
+  SA_TRY(check_ptr(v, "v", 16, need));
+  SA_TRY(check_ptr(o, "o", 16, need));
+  SA_TRY(check_ptr(lse, "lse", 4, need));
+  SA_TRY(check_ptr(s, "s", 4, false));
+  SA_TRY(check_ptr(desc->learnable_sink, "learnable_sink", 4, false));
+  SA_TRY(check_ptr(desc->block_indices, "block_indices", 4, false));
+  if (workspace_bytes < sink_attn_fwd_workspace_size(desc))
+    return fail(SINK_ATTN_WORKSPACE_TOO_SMALL, "workspace too small");
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_check_bwd(const sink_attn_prefill_desc* desc, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const void* dout,
+                        const void* dq, const void* dk, const void* dv, const float* dsink,
+                        size_t workspace_bytes) {
+  SA_TRY(check_prefill_desc(desc));
+  const bool need = desc->total_tokens > 0;
+  SA_TRY(check_ptr(q, "q", 16, need));
+  SA_TRY(check_ptr(k, "k", 16, need));
+  SA_TRY(check_ptr(v, "v", 16, need));
+  SA_TRY(check_ptr(o, "o", 16, need));
+  SA_TRY(check_ptr(lse, "lse", 4, need));
+  SA_TRY(check_ptr(dout, "dout", 16, need));
+  SA_TRY(check_ptr(dq, "dq", 16, need));
+  SA_TRY(check_ptr(dk, "dk", 16, need));
+  SA_TRY(check_ptr(dv, "dv", 16, need));
+  SA_TRY(check_ptr(desc->learnable_sink, "learnable_sink", 4, false));
+  SA_TRY(check_ptr(desc->block_indices, "block_indices", 4, false));
+  if (desc->learnable_sink != nullptr && dsink == nullptr)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "dsink is NULL while learnable_sink is set");
+  if (desc->learnable_sink == nullptr && dsink != nullptr)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "dsink is set while learnable_sink is NULL");
+  SA_TRY(check_ptr(dsink, "dsink", 4, false));
+  if (workspace_bytes < sink_attn_bwd_workspace_size(desc))
+    return fail(SINK_ATTN_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu", workspace_bytes,
+                sink_attn_bwd_workspace_size(desc));
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_check_decode(const sink_attn_decode_desc* desc, const void* q, const void* k_cache,
+                           const void* v_cache, const void* o, const float* lse, const float* s,
+                           size_t workspace_bytes) {
+  SA_TRY(check_decode_desc(desc));
+  const bool need = desc->batch > 0;
+  SA_TRY(check_ptr(q, "q", 16, need));
+  SA_TRY(check_ptr(k_cache, "k_cache", 16, need));
+  SA_TRY(check_ptr(v_cache, "v_cache", 16, need));
+  SA_TRY(check_ptr(o, "o", 16, need));
+  SA_TRY(check_ptr(lse, "lse", 4, need));
+  SA_TRY(check_ptr(s, "s", 4, false));
+  SA_TRY(check_ptr(desc->learnable_sink, "learnable_sink", 4, false));
+  SA_TRY(check_ptr(desc->cache_seqlens, "cache_seqlens", 4, false));
+  if (workspace_bytes < sink_attn_decode_workspace_size(desc))
+    return fail(SINK_ATTN_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu", workspace_bytes,
+                sink_attn_decode_workspace_size(desc));
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_fwd(const sink_attn_prefill_desc* desc, const void* q, const void* k, const void* v,
+                  void* o, float* lse, float* s, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  try {
+    SA_TRY(sink_attn_check_fwd(desc, q, k, v, o, lse, s, workspace_bytes));
+    (void)workspace;
+    const sa::Prefill p = to_prefill(desc);
+    if (p.total == 0) return SINK_ATTN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::fwd_mfma_supported(p) ? sa::launch_fwd_mfma(p, q, k, v, o, lse, s, st)
+                                             : sa::launch_fwd_generic(p, q, k, v, o, lse, s, st);
+    return hip_status(e, "sink_attn_fwd launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_fwd");
+  }
+}
+
+int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void* k, const void* v,
+                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  float* dsink, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    SA_TRY(sink_attn_check_bwd(desc, q, k, v, o, lse, dout, dq, dk, dv, dsink, workspace_bytes));
+    const sa::Prefill p = to_prefill(desc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.total == 0) {
+      if (dsink != nullptr) {
+        // No rows: dsink is an empty sum.
+        hipError_t e = sa::launch_fill_zero(dsink, p.hq, st);
+        return hip_status(e, "sink_attn_bwd dsink clear");
+      }
+      return SINK_ATTN_OK;
+    }
+    const BwdLayout lay = bwd_layout(p);
+    char* base = static_cast<char*>(workspace);
+    sa::BwdWork w;
+    w.delta = reinterpret_cast<float*>(base + lay.delta);
+    w.lnew = reinterpret_cast<float*>(base + lay.lnew);
+    w.dsink_terms = reinterpret_cast<float*>(base + lay.terms);
+    w.dq_acc = reinterpret_cast<float*>(base + lay.dq_acc);
+    w.dk_acc = reinterpret_cast<float*>(base + lay.dk_acc);
+    w.dv_acc = reinterpret_cast<float*>(base + lay.dv_acc);
+    w.csr_off = reinterpret_cast<int32_t*>(base + lay.csr_off);
+    w.csr_idx = reinterpret_cast<int32_t*>(base + lay.csr_idx);
+    const bool mfma = sa::bwd_mfma_supported(p);
+    hipError_t e;
+    if (mfma) {
+      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dq=*/true, /*zero_dkv=*/true, st);
+      if (e == hipSuccess && p.blocks != nullptr) e = sa::launch_block_csr(p, w, st);
+      if (e == hipSuccess) e = sa::launch_bwd_mfma(p, q, k, v, dout, w, dk, dv, st);
+      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dq, dk, dv, true, false, st);
+    } else {
+      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, false, true, st);
+      if (e == hipSuccess) e = sa::launch_bwd_generic(p, q, k, v, dout, w, dq, st);
+      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dq, dk, dv, false, true, st);
+    }
+    return hip_status(e, "sink_attn_bwd launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_bwd");
+  }
+}
+
+int sink_attn_decode(const sink_attn_decode_desc* desc, const void* q, const void* k_cache,
+                     const void* v_cache, void* o, float* lse, float* s, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  try {
+    SA_TRY(sink_attn_check_decode(desc, q, k_cache, v_cache, o, lse, s, workspace_bytes));
+    const sa::Decode p = to_decode(desc);
+    if (p.batch == 0) return SINK_ATTN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_decode(p, q, k_cache, v_cache, o, lse, s,
+                                     static_cast<float*>(workspace), st);
+    return hip_status(e, "sink_attn_decode launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_decode");
+  }
+}
+
+int sink_attn_debug_visit_map(const sink_attn_prefill_desc* desc, uint8_t* out, size_t out_bytes,
+                              void* stream) {
+  try {
+    SA_TRY(check_prefill_desc(desc));
+    if (desc->max_seqlen > 4096)
+      return fail(SINK_ATTN_UNSUPPORTED, "visit map needs max_seqlen <= 4096");
+    if (desc->total_tokens == 0) return SINK_ATTN_OK;
+    SA_TRY(check_ptr(out, "out", 1, true));
+    const size_t need = static_cast<size_t>(desc->num_kv_heads) * desc->max_seqlen *
+                        static_cast<size_t>(desc->total_tokens);
+    if (out_bytes < need)
+      return fail(SINK_ATTN_INVALID_ARGUMENT, "out_bytes %zu < Hkv*max_seqlen*total_tokens = %zu",
+                  out_bytes, need);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_fill_zero_bytes(out, out_bytes, st);
+    if (e == hipSuccess) e = sa::launch_visit_map(to_prefill(desc), out, st);
+    return hip_status(e, "sink_attn_debug_visit_map launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_debug_visit_map");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+"""Shared helpers of the GPU parity tests: device copies of drawn workloads,
+calls through the binding, and the tolerance checks."""
+import numpy as np
+import torch
+
+import oracle
+import streamingllm_sink_attn_amd as sa
+from streamingllm_sink_attn_amd import workloads as W
+
+DEV = "cuda"
+
+# bf16 inputs, float32 accumulation
+TOL_BF16 = dict(o_max=2e-2, o_mean=2e-3, lse=1e-3, s=1e-3, grad=5e-2, dsink_rel=1e-2)
+# float32 storage
+TOL_F32 = dict(o_max=1e-4, o_mean=1e-5, lse=1e-4, s=1e-4, grad=1e-4, dsink_rel=1e-4)
+
+
+def tol_for(dtype):
+    return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+def dev(t: W.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(t.f32)).to(DEV)
+
+
+def host(x: torch.Tensor) -> np.ndarray:
+    return x.detach().float().cpu().numpy().astype(np.float64)
+
+
+def prefill_args(wl: W.Prefill):
+    q, k, v = dev(wl.q, wl.dtype), dev(wl.k, wl.dtype), dev(wl.v, wl.dtype)
+    cu = torch.from_numpy(wl.cu_seqlens).to(DEV)
+    bi = torch.from_numpy(wl.block_indices).to(DEV) if wl.block_indices is not None else None
+    sink = torch.from_numpy(wl.sink).to(DEV) if wl.sink is not None else None
+    return q, k, v, cu, bi, sink
+
+
+def run_fwd(wl: W.Prefill, args=None):
+    q, k, v, cu, bi, sink = args if args is not None else prefill_args(wl)
+    o, lse, s = sa.fwd(q, k, v, cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+    torch.cuda.synchronize()
+    return o, lse, s
+
+
+def run_bwd(wl: W.Prefill, o, lse, args=None):
+    q, k, v, cu, bi, sink = args if args is not None else prefill_args(wl)
+    do = dev(wl.do, wl.dtype)
+    g = sa.bwd(q, k, v, o, lse, do, cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_kwargs(wl: W.Prefill):
+    return dict(n_sink=wl.n_sink, window=wl.window, block_indices=wl.block_indices,
+                block_size=wl.block_size, sink=wl.sink)
+
+
+def assert_lse(got, want, tol, what="lse"):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    ninf_w = np.isneginf(want)
+    ninf_g = np.isneginf(got)
+    assert np.array_equal(ninf_w, ninf_g), f"{what}: -inf pattern differs ({ninf_w.sum()} vs {ninf_g.sum()})"
+    fin = ~ninf_w
+    if fin.any():
+        err = np.max(np.abs(got[fin] - want[fin]))
+        assert err <= tol, f"{what}: max abs err {err:.3e} > {tol}"
+
+
+def assert_out(got, want, tol, what="O"):
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    mx = float(err.max()) if err.size else 0.0
+    mean = float(err.mean()) if err.size else 0.0
+    assert mx <= tol["o_max"], f"{what}: max abs err {mx:.3e} > {tol['o_max']}"
+    assert mean <= tol["o_mean"], f"{what}: mean abs err {mean:.3e} > {tol['o_mean']}"
+
+
+def assert_grad(got, want, tol, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert err <= tol["grad"], f"{what}: max abs err {err:.3e} > {tol['grad']}"
+
+
+def assert_dsink(got, want, tol):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    scale = max(float(np.max(np.abs(want))), 1e-6)
+    rel = float(np.max(np.abs(got - want))) / scale
+    assert rel <= tol["dsink_rel"], f"dsink: relative err {rel:.3e} > {tol['dsink_rel']}"
+
+
+def check_fwd_full(wl: W.Prefill, out):
+    o, lse, s = out
+    tol = tol_for(wl.dtype)
+    ro, rl, rs = oracle.fwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, **oracle_kwargs(wl))
+    assert_out(host(o), ro, tol)
+    assert_lse(host(lse), rl, tol["lse"])
+    if s is not None:
+        err = float(np.max(np.abs(host(s) - rs))) if rs.size else 0.0
+        assert err <= tol["s"], f"s: max abs err {err:.3e}"
+    return ro, rl, rs
+

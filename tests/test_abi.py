@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+its pure-host validation returns the documented status codes.  No call here
+launches a kernel; pointers are fake, aligned addresses that are never read."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from streamingllm_sink_attn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sink_attn.h")
+
+FAKE = 0x10000          # aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sink_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGS), "binding signatures must cover the header"
+
+
+def _desc(**kw):
+    d = dict(cu_seqlens=FAKE, batch=2, total_tokens=100, max_seqlen=60, num_q_heads=8,
+             num_kv_heads=2, head_dim=128, dtype=B.BF16, softmax_scale=0.088, n_sink=4,
+             window=32, block_indices=None, num_q_blocks=0, block_size=64, max_blocks=0,
+             learnable_sink=FAKE)
+    d.update(kw)
+    return B.PrefillDesc(**d)
+
+
+def check_fwd(desc, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, s=FAKE, ws=0):
+    return B.lib().sink_attn_check_fwd(ctypes.byref(desc), q, k, v, o, lse, s, ws)
+
+
+def check_bwd(desc, dsink=FAKE, ws=None, **kw):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
+    p.update(kw)
+    if ws is None:
+        ws = B.lib().sink_attn_bwd_workspace_size(ctypes.byref(desc))
+    return B.lib().sink_attn_check_bwd(ctypes.byref(desc), p["q"], p["k"], p["v"], p["o"], p["lse"],
+                                       p["dout"], p["dq"], p["dk"], p["dv"], dsink, ws)
+
+
+def test_check_fwd_ok_and_errors():
+    assert check_fwd(_desc()) == B.OK
+    assert check_fwd(_desc(), s=None) == B.OK                        # s optional
+    assert B.lib().sink_attn_check_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(), q=None) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(), lse=None) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(), q=FAKE + 2) == B.INVALID_ARGUMENT       # misaligned
+    assert check_fwd(_desc(num_q_heads=6, num_kv_heads=4)) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(num_kv_heads=0)) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(head_dim=100)) == B.UNSUPPORTED
+    assert check_fwd(_desc(head_dim=512)) == B.UNSUPPORTED
+    assert check_fwd(_desc(dtype=7)) == B.UNSUPPORTED
+    assert check_fwd(_desc(softmax_scale=0.0)) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(softmax_scale=float("nan"))) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(n_sink=-1)) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(batch=-1)) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(cu_seqlens=None)) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(max_seqlen=0)) == B.INVALID_ARGUMENT
+    # empty problem: nothing required
+    assert check_fwd(_desc(total_tokens=0, batch=0, cu_seqlens=None), q=None, k=None, v=None,
+                     o=None, lse=None) == B.OK
+    # block lists
+    bd = dict(block_indices=FAKE, num_q_blocks=2, max_blocks=3)
+    assert check_fwd(_desc(**bd)) == B.OK
+    assert check_fwd(_desc(**dict(bd, block_size=32))) == B.UNSUPPORTED
+    assert check_fwd(_desc(**dict(bd, max_blocks=0))) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(**dict(bd, num_q_blocks=1))) == B.INVALID_ARGUMENT
+    assert check_fwd(_desc(**dict(bd, max_seqlen=10**6, total_tokens=10**6, num_q_blocks=20000))) == B.UNSUPPORTED
+
+
+def test_last_error_message_and_strerror():
+    check_fwd(_desc(head_dim=100))
+    assert "head_dim" in B.lib().sink_attn_last_error().decode()
+    for st in range(5):
+        assert B.lib().sink_attn_strerror(st)
+    assert B.lib().sink_attn_strerror(99) == b"unknown status"
+
+
+def test_check_bwd_dsink_rules_and_workspace():
+    d = _desc()
+    assert check_bwd(d) == B.OK
+    assert check_bwd(d, dsink=None) == B.INVALID_ARGUMENT             # sink set, dsink missing
+    assert check_bwd(_desc(learnable_sink=None), dsink=FAKE) == B.INVALID_ARGUMENT
+    assert check_bwd(_desc(learnable_sink=None), dsink=None) == B.OK
+    need = B.lib().sink_attn_bwd_workspace_size(ctypes.byref(d))
+    assert need >= 3 * 100 * 8 * 4
+    assert check_bwd(d, ws=need - 1) == B.WORKSPACE_TOO_SMALL
+    assert check_bwd(d, dq=None) == B.INVALID_ARGUMENT
+    assert check_bwd(d, dout=FAKE + 8) == B.INVALID_ARGUMENT
+
+
+def _ddesc(**kw):
+    d = dict(cache_seqlens=None, batch=4, slots=128, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             dtype=B.BF16, softmax_scale=0.088, learnable_sink=FAKE, num_splits=0)
+    d.update(kw)
+    return B.DecodeDesc(**d)
+
+
+def test_check_decode():
+    L = B.lib()
+
+    def chk(desc, ws=None, **kw):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, s=FAKE)
+        p.update(kw)
+        if ws is None:
+            ws = L.sink_attn_decode_workspace_size(ctypes.byref(desc))
+        return L.sink_attn_check_decode(ctypes.byref(desc), p["q"], p["k"], p["v"], p["o"], p["lse"],
+                                        p["s"], ws)
+    assert chk(_ddesc()) == B.OK
+    assert chk(_ddesc(), s=None) == B.OK
+    assert chk(_ddesc(slots=0)) == B.INVALID_ARGUMENT
+    assert chk(_ddesc(num_splits=-1)) == B.INVALID_ARGUMENT
+    assert chk(_ddesc(num_splits=1000)) == B.INVALID_ARGUMENT
+    assert chk(_ddesc(head_dim=12)) == B.UNSUPPORTED
+    assert chk(_ddesc(), k=None) == B.INVALID_ARGUMENT
+    need = L.sink_attn_decode_workspace_size(ctypes.byref(_ddesc()))
+    if need:
+        assert chk(_ddesc(), ws=need - 1) == B.WORKSPACE_TOO_SMALL
+
+
+def test_prefill_path_selection():
+    L = B.lib()
+    assert L.sink_attn_prefill_path(ctypes.byref(_desc())) == 1             # bf16, D=128
+    assert L.sink_attn_prefill_path(ctypes.byref(_desc(head_dim=64))) == 0
+    assert L.sink_attn_prefill_path(ctypes.byref(_desc(dtype=B.F32))) == 0
+    assert L.sink_attn_prefill_path(ctypes.byref(_desc(head_dim=100))) == -1
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libsinkattn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
