@@ -108,6 +108,36 @@ def bench_gqa_prefill(torch, sa, W, steps, warmup):
                 tflops=tflops, wl=wl)
 
 
+def bench_decode(torch, sa, W, steps, warmup):
+    """StreamingLLM decode: 128 sequences x 4096-slot cache, Hq=64, Hkv=8.
+    Two cache copies alternate so no call finds the previous one's bytes in
+    the on-die caches.  Bytes count each valid K/V slot once plus Q, O, lse, s."""
+    wl = W.streaming_decode()
+    q = _dev_bf16(wl.q, torch)
+    kc = [_dev_bf16(wl.k_cache, torch)]
+    vc = [_dev_bf16(wl.v_cache, torch)]
+    kc.append(torch.roll(kc[0], 1, dims=1).contiguous())
+    vc.append(torch.roll(vc[0], 1, dims=1).contiguous())
+    sink = torch.from_numpy(wl.sink).cuda()
+    o = torch.empty_like(q)
+    nbytes = (2 * wl.batch * wl.slots * wl.hkv * wl.d * 2 + 2 * wl.batch * wl.hq * wl.d * 2
+              + 2 * wl.batch * wl.hq * 4)
+    it = [0]
+
+    def step():
+        i = it[0] & 1
+        it[0] += 1
+        sa.decode(q, kc[i], vc[i], None, wl.scale, sink, out=o)
+
+    ms, wall_ms = Timer(torch).run(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "streaming_decode", "unit": "GB/s", "value": round(gbs, 1),
+            "ms_per_step": round(ms, 4), "bytes_per_step": nbytes,
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "config": {"batch": wl.batch, "slots": wl.slots, "hq": wl.hq, "hkv": wl.hkv,
+                       "head_dim": wl.d}}
+
+
 def cpu_baseline(W, budget_s=15.0):
     """The float64 oracle on whole (sample, head) units of the same workload,
     until about budget_s seconds of CPU work; reported in TFLOP/s counted the
@@ -180,6 +210,14 @@ def main():
                    "sink": "learnable", "flops_per_step": head["flops"]},
         "roofline": roofline,
     }
+    also = []
+    for fn in (bench_decode,):
+        try:
+            also.append(fn(torch, sa, W, args.steps, args.warmup))
+        except Exception as e:  # noqa: BLE001 - report, keep the headline
+            also.append({"workload": fn.__name__, "error": repr(e)})
+        torch.cuda.empty_cache()
+    line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(line), flush=True)

@@ -1,4 +1,30 @@
-// Decode dispatch.
+// Decode against a rolling KV cache: split-KV on matrix cores, then a merge of
+// the splits by their log-sum-exp with the sink epilogue.
+//
+// The cache of each sequence is an unordered set of slots (a ring buffer keeps
+// the first tokens and the recent window in any slot order: "Attention Sink"
+// (lijianxiong.space), H2O circular cache; StreamingLLM's fixed first-token
+// segment plus sliding window: "What is Attention Sink? ... StreamingLLM"
+// (model.playoffer.cn)).  No mask applies beyond cache_seqlens.  The sink is
+// the output scale s = sigma(L_orig - a_h) ("Attention Sink, Learnable Sink
+// and dsink" s4), applied once after the merge.
+//
+// Split kernel (bf16, head_dim 128), one workgroup per (sequence b, KV head g,
+// head group, split):
+//   * 4 wavefronts stream disjoint 32-slot chunks of the split.  The query
+//     heads of the group (up to 16) form the N side of
+//     v_mfma_f32_16x16x32_bf16; S^T = K Q^T puts one head per lane column.
+//   * K goes from HBM straight into the MFMA A-operand registers: lane
+//     (slot, quarter) reads 16 bytes per k-step and the four quarters of a
+//     slot read one contiguous 64-byte piece of its row.  The next chunk's K
+//     is in flight while the current chunk computes.
+//   * V is staged through a per-wavefront LDS buffer (rows XOR-swizzled in
+//     16-byte chunks) and read back transposed with ds_read_b64_tr_b16, which
+//     gives each lane one dim at 4 slots: the A operand of O^T += V^T P^T.
+//   * The 4 wavefronts merge (m, l, acc) in LDS; the workgroup writes one
+//     partial per (b, head, split) to the workspace.
+// Merge kernel: M = max_k m_k, l = sum_k e^{m_k - M} l_k, L_orig = M + ln l,
+// O = s * sum_k e^{m_k - M} acc_k / l.
 #include "common.cuh"
 
 namespace sa {
@@ -6,20 +32,332 @@ namespace sa {
 hipError_t launch_decode_generic(const Decode& p, const void* q, const void* kc, const void* vc,
                                  void* o, float* lse, float* s, hipStream_t st);
 
-int decode_auto_splits(const Decode& p) {
-  (void)p;
-  return 1;
+namespace dec128 {
+
+constexpr int D = 128;
+constexpr int CH = 32;            // slots per chunk
+constexpr int NW = 4;             // wavefronts per workgroup
+constexpr int HN = 16;            // query heads per workgroup (N of the MFMA)
+constexpr int VBUF = CH * D;      // bf16 elements of one V chunk buffer (8 KB)
+constexpr float kRescaleLog2 = 8.f;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte chunk swizzle of a V row: spreads the 4 slots x 4 chunks that one
+// transposed read touches over distinct banks.
+__device__ __forceinline__ int vswz(int row) {
+  const int r = row & 15;
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<uint16_t*>(lds_ptr)));
+}
+
+__global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
+                                                       const uint16_t* __restrict__ Q,
+                                                       const uint16_t* __restrict__ KC,
+                                                       const uint16_t* __restrict__ VC,
+                                                       float* __restrict__ ws) {
+  // Per-wavefront double-buffered V chunks; after the loop the same memory
+  // holds the wavefronts' partial results for the merge.
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][2][VBUF];
+  static_assert(sizeof(float) * NW * HN * (D + 2) <= sizeof(uint16_t) * NW * 2 * VBUF, "merge fits");
+  float (*mbuf)[HN][D + 2] = reinterpret_cast<float (*)[HN][D + 2]>(&vbuf[0][0][0]);
+
+  // grid: x = split (fastest), y = KV head * head groups, z = sequence
+  const int split = blockIdx.x;
+  const int g = blockIdx.y / nhg;
+  const int hg = blockIdx.y % nhg;
+  const int b = blockIdx.z;
+  const int G = p.hq / p.hkv;
+  const int h0 = g * G + hg * HN;                    // first query head of the group
+  const int nh = min(HN, G - hg * HN);               // heads in this workgroup
+  const int n = p.cache_seqlens ? min(p.cache_seqlens[b], p.slots) : p.slots;
+  const int per = (p.slots + p.splits - 1) / p.splits;
+  const int s0 = split * per;
+  const int s1 = min(n, s0 + per);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+
+  // Q^T as B operand: lane (head l16, quarter gq), k-step ks: dims ks*32 + gq*8.
+  bf16x8 qf[4];
+  {
+    const bool ok = l16 < nh;
+    const uint16_t* src = Q + (static_cast<size_t>(b) * p.hq + h0 + (ok ? l16 : 0)) * D + gq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32))
+                  : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  const size_t row_stride = static_cast<size_t>(p.hkv) * D;
+  const uint16_t* Kb = KC + (static_cast<size_t>(b) * p.slots * p.hkv + g) * D;
+  const uint16_t* Vb = VC + (static_cast<size_t>(b) * p.slots * p.hkv + g) * D;
+  const float c = p.scale * kLog2e;
+  const float thr = kRescaleLog2 / c;
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -kInf, lpart = 0.f;
+
+  // Chunks of this wavefront: start at s0 + 32*(w + 4*i).
+  const int nchunks_total = (s1 > s0) ? (s1 - s0 + CH - 1) / CH : 0;
+  const int my_first = w;
+  u32x4 kf[2][4], kn[2][4];     // current / next chunk K fragments [mt][ks]
+  u32x4 vr[8];                  // next chunk V rows, 8 x 16 B per lane
+
+  auto load_k = [&](int cs, u32x4 (&dst)[2][4]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      int slot = cs + mt * 16 + l16;
+      slot = slot < p.slots ? slot : p.slots - 1;
+      const uint16_t* src = Kb + static_cast<size_t>(slot) * row_stride + gq * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
+    }
+  };
+  auto load_v = [&](int cs) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int slot = cs + (lane >> 4) + 4 * i;
+      slot = slot < p.slots ? slot : p.slots - 1;
+      vr[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(slot) * row_stride + l16 * 8);
+    }
+  };
+  auto store_v = [&](uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (lane >> 4) + 4 * i;
+      const int pc = l16 ^ vswz(row);
+      *reinterpret_cast<u32x4*>(buf + row * D + pc * 8) = vr[i];
+    }
+  };
+
+  int ci = my_first;
+  int cur = 0;
+  if (ci < nchunks_total) {
+    const int cs = s0 + CH * ci;
+    load_k(cs, kf);
+    load_v(cs);
+    store_v(vbuf[w][0]);
+  }
+  while (ci < nchunks_total) {
+    const int cs = s0 + CH * ci;
+    const int cn = ci + NW;
+    const bool has_next = cn < nchunks_total;
+    if (has_next) {
+      load_k(s0 + CH * cn, kn);
+      load_v(s0 + CH * cn);
+    }
+    // S^T = K Q^T for 32 slots (2 M-tiles of 16) x 16 heads.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc[mt] = mfma16(__builtin_bit_cast(bf16x8, kf[mt][ks]), qf[ks], sacc[mt]);
+    }
+    // Mask slots past the split or the valid length.  Element i of lane
+    // (l16, gq) in M-tile mt is slot cs + 16mt + 4gq + i, head l16.
+    if (cs + CH > s1) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (cs + 16 * mt + 4 * gq + i >= s1) sacc[mt][i] = -kInf;
+    }
+    float mx = -kInf;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[mt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__ballot(mx > mrun + thr) != 0) {
+      const float mnew = fmaxf(mrun, mx);
+      const float f = (mrun == -kInf) ? 0.f : __builtin_amdgcn_exp2f((mrun - mnew) * c);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= f;
+      lpart *= f;
+      mrun = mnew;
+    }
+    const float mb = (mrun == -kInf) ? 0.f : mrun * c;
+    float pv[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c, -mb));
+        pv[mt * 4 + i] = e;
+        lpart += e;
+      }
+    // B operand: logical k slot t of quarter gq = slot 16*(t/4) + 4gq + t%4.
+    const bf16x8 pf = __builtin_bit_cast(
+        bf16x8, u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                      pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+    // O^T += V^T P^T: 8 dim tiles of 16.  Transposed reads: lane s = 4r + q of
+    // quarter gq reads slot 4gq + r (and 16 + 4gq + r), dims dt*16 + 4q..+4.
+    const uint16_t* vb = vbuf[w][cur];
+    const int r = l16 >> 2, q4 = l16 & 3;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int lc = dt * 2 + (q4 >> 1);
+      const int off = (q4 & 1) * 4;
+      const int r0 = 4 * gq + r, r1 = 16 + 4 * gq + r;
+      const i16x4 a0 = ds_read_tr(vb + r0 * D + ((lc ^ vswz(r0)) * 8) + off);
+      const i16x4 a1 = ds_read_tr(vb + r1 * D + ((lc ^ vswz(r1)) * 8) + off);
+      const bf16x8 af = __builtin_bit_cast(
+          bf16x8, u32x4{__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                        __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]});
+      oacc[dt] = mfma16(af, pf, oacc[dt]);
+    }
+    if (has_next) {
+      store_v(vbuf[w][cur ^ 1]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = kn[mt][ks];
+    }
+    cur ^= 1;
+    ci = cn;
+  }
+
+  // Merge the 4 wavefronts.  Per head: m (same on the 4 quarters), l summed
+  // over quarters, acc dims dt*16 + 4gq + i.
+  lpart += __shfl_xor(lpart, 16);
+  lpart += __shfl_xor(lpart, 32);
+  __syncthreads();                 // every wavefront is done with its V buffers
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mbuf[w][l16][dt * 16 + 4 * gq + i] = oacc[dt][i];
+  if (gq == 0) {
+    mbuf[w][l16][D] = mrun;
+    mbuf[w][l16][D + 1] = lpart;
+  }
+  __syncthreads();
+  {
+    const int hh = tid >> 4;          // head in group (16)
+    const int d0 = (tid & 15) * 8;    // 8 dims
+    if (hh < nh) {
+      float M = -kInf;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mbuf[ww][hh][D]);
+      float wgt[NW];
+      float lt = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = mbuf[ww][hh][D];
+        wgt[ww] = (mw == -kInf) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
+        lt += wgt[ww] * mbuf[ww][hh][D + 1];
+      }
+      float* dst = ws + ((static_cast<size_t>(b) * p.hq + h0 + hh) * p.splits + split) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) a += wgt[ww] * mbuf[ww][hh][d0 + e];
+        dst[d0 + e] = a;
+      }
+      if ((tid & 15) == 0) {
+        dst[D] = (M == -kInf) ? -kInf : M * p.scale;   // natural-log units
+        dst[D + 1] = lt;
+      }
+    }
+  }
+}
+
+}  // namespace dec128
+
+// Merge of the splits (any head_dim): one workgroup per (sequence, head).
+template <typename T>
+__global__ __launch_bounds__(128) void decode_merge_kernel(Decode p, const float* __restrict__ ws,
+                                                           void* o, float* lse, float* s_out) {
+  const int b = blockIdx.x / p.hq;
+  const int h = blockIdx.x % p.hq;
+  const int D = p.d;
+  const float* base = ws + (static_cast<size_t>(b) * p.hq + h) * p.splits * (D + 2);
+  float M = -kInf;
+  for (int k = 0; k < p.splits; ++k) M = fmaxf(M, base[k * (D + 2) + D]);
+  float l = 0.f;
+  for (int k = 0; k < p.splits; ++k) {
+    const float mk = base[k * (D + 2) + D];
+    if (mk != -kInf) l += __expf(mk - M) * base[k * (D + 2) + D + 1];
+  }
+  const bool has_sink = p.sink != nullptr;
+  float L_orig, s_val, mul;
+  if (l > 0.f) {
+    L_orig = M + __logf(l);
+    s_val = has_sink ? 1.f / (1.f + __expf(p.sink[h] - L_orig)) : 1.f;
+    mul = s_val / l;
+  } else {
+    L_orig = -kInf;
+    s_val = has_sink ? 0.f : 1.f;
+    mul = 0.f;
+  }
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float a = 0.f;
+    for (int k = 0; k < p.splits; ++k) {
+      const float mk = base[k * (D + 2) + D];
+      if (mk != -kInf) a += __expf(mk - M) * base[k * (D + 2) + d];
+    }
+    Elem<T>::store(o, (static_cast<size_t>(b) * p.hq + h) * D + d, a * mul);
+  }
+  if (threadIdx.x == 0) {
+    lse[static_cast<size_t>(b) * p.hq + h] = L_orig;
+    if (s_out) s_out[static_cast<size_t>(b) * p.hq + h] = s_val;
+  }
 }
 
 bool decode_mfma_supported(const Decode& p) {
-  (void)p;
-  return false;
+  return p.dtype == SINK_ATTN_BF16 && p.d == dec128::D;
+}
+
+int decode_auto_splits(const Decode& p) {
+  // Enough workgroups to keep every CU streaming (about 8 per CU), but no
+  // split shorter than 4 chunks per wavefront.
+  const int G = p.hq / p.hkv;
+  const long long units = static_cast<long long>(p.batch) * p.hkv * ((G + dec128::HN - 1) / dec128::HN);
+  if (units <= 0) return 1;
+  long long want = (2048 + units - 1) / units;
+  const long long max_by_len = p.slots / (dec128::CH * dec128::NW * 4);
+  if (want > max_by_len) want = max_by_len;
+  if (want < 1) want = 1;
+  if (want > 64) want = 64;
+  return static_cast<int>(want);
 }
 
 hipError_t launch_decode(const Decode& p, const void* q, const void* kc, const void* vc, void* o,
                          float* lse, float* s, float* ws, hipStream_t st) {
-  (void)ws;
-  return launch_decode_generic(p, q, kc, vc, o, lse, s, st);
+  if (!decode_mfma_supported(p)) return launch_decode_generic(p, q, kc, vc, o, lse, s, st);
+  const int G = p.hq / p.hkv;
+  const int nhg = (G + dec128::HN - 1) / dec128::HN;
+  dim3 grid(p.splits, p.hkv * nhg, p.batch);
+  hipLaunchKernelGGL(dec128::split_kernel, grid, dim3(256), 0, st, p, nhg,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                     static_cast<const uint16_t*>(vc), ws);
+  hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3(p.batch * p.hq), dim3(128), 0, st, p, ws, o,
+                     lse, s);
+  return hipGetLastError();
 }
 
 }  // namespace sa

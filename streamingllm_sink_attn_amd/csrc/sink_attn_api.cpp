@@ -132,6 +132,7 @@ int check_decode_desc(const sink_attn_decode_desc* d) {
     return fail(SINK_ATTN_UNSUPPORTED, "head_dim %d not supported", d->head_dim);
   if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
     return fail(SINK_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (d->batch > 65535) return fail(SINK_ATTN_UNSUPPORTED, "batch > 65535");
   if (d->num_splits < 0 || d->num_splits > 256)
     return fail(SINK_ATTN_INVALID_ARGUMENT, "num_splits must be in [0, 256]");
   return SINK_ATTN_OK;

@@ -231,3 +231,20 @@ def test_decode_variants(name, splits):
     assert_out(host(o), ro, tol)
     assert_lse(host(lse), rl, tol["lse"])
     assert float(np.max(np.abs(host(s) - rs))) <= tol["s"]
+
+
+def test_decode_permutation_and_split_invariance():
+    """Slots are an unordered set and the split merge is exact: permuting the
+    cache or changing num_splits changes the result only by rounding."""
+    wl = _dwl("d128_g8", seed=9)
+    wl = W.make_decode("perm", 4, 1000, 16, 2, 128, seed=9)
+    ro, rl, rs = oracle.decode(wl.q.f32, wl.k_cache.f32, wl.v_cache.f32, wl.scale, sink=wl.sink)
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(wl.slots)).to(DEV)
+    tol = tol_for("bf16")
+    for splits in (1, 2, 4, 7, 8):
+        for pm in (None, perm):
+            _announce(f"decode invariance splits={splits} perm={pm is not None}")
+            o, lse, s = run_decode(wl, splits, pm)
+            assert_out(host(o), ro, tol)
+            assert_lse(host(lse), rl, tol["lse"])
+            assert float(np.max(np.abs(host(s) - rs))) <= tol["s"]
