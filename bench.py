@@ -108,6 +108,61 @@ def bench_gqa_prefill(torch, sa, W, steps, warmup):
                 tflops=tflops, wl=wl)
 
 
+def _fwd_bwd_leg(torch, sa, wl, pairs, name, steps, warmup, cfg):
+    """Times one forward + backward per step; FLOPs are 14*D per valid pair
+    (4*D forward, 10*D backward), and fwd / bwd are also timed alone."""
+    q, k, v = _dev_bf16(wl.q, torch), _dev_bf16(wl.k, torch), _dev_bf16(wl.v, torch)
+    do = _dev_bf16(wl.do, torch)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    sink = torch.from_numpy(wl.sink).cuda()
+    bi = torch.from_numpy(wl.block_indices).cuda() if wl.block_indices is not None else None
+    o = torch.empty_like(q)
+    state = {}
+
+    def fwd():
+        state["out"] = sa.fwd(q, k, v, cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink,
+                              return_s=True, out=o)
+
+    def bwd():
+        _, lse, _ = state["out"]
+        sa.bwd(q, k, v, o, lse, do, cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+
+    def step():
+        fwd()
+        bwd()
+
+    T = Timer(torch)
+    ms, _ = T.run(step, steps, warmup)
+    ms_f, _ = T.run(fwd, steps, 2)
+    ms_b, _ = T.run(bwd, steps, 2)
+    f_all, f_f, f_b = 14.0 * wl.d * pairs, 4.0 * wl.d * pairs, 10.0 * wl.d * pairs
+    tf = f_all / (ms * 1e-3) / 1e12
+    return {"workload": name, "unit": "TFLOP/s", "value": round(tf, 2),
+            "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_step": round(ms, 4),
+            "flops_per_step": f_all, "valid_pairs": pairs,
+            "fwd": {"ms": round(ms_f, 4), "tflops": round(f_f / (ms_f * 1e-3) / 1e12, 2)},
+            "bwd": {"ms": round(ms_b, 4), "tflops": round(f_b / (ms_b * 1e-3) / 1e12, 2)},
+            "config": cfg}
+
+
+def bench_streaming_prefill(torch, sa, W, steps, warmup):
+    """8 varlen samples (sum 32768), Hq=32, Hkv=8, D=128, n_sink=4, window=1024."""
+    wl = W.streaming_prefill()
+    pairs = _counts_window(wl.lengths, wl.n_sink, wl.window) * wl.hq
+    return _fwd_bwd_leg(torch, sa, wl, pairs, "streaming_prefill_fwd_bwd", steps, warmup,
+                        {"lengths": [int(x) for x in wl.lengths], "hq": wl.hq, "hkv": wl.hkv,
+                         "head_dim": wl.d, "n_sink": wl.n_sink, "window": wl.window})
+
+
+def bench_block_sparse(torch, sa, W, steps, warmup):
+    """4 x 16384, Hq=64, Hkv=8, D=128, 64-token blocks: first + 15 random + diagonal."""
+    wl = W.block_sparse()
+    pairs = _counts_blocks(wl.lengths, wl.block_indices, wl.hkv, wl.hq)
+    return _fwd_bwd_leg(torch, sa, wl, pairs, "block_sparse_fwd_bwd", steps, warmup,
+                        {"batch": wl.batch, "seq_len": int(wl.lengths[0]), "hq": wl.hq,
+                         "hkv": wl.hkv, "head_dim": wl.d, "blocks_per_row": 17})
+
+
 def bench_decode(torch, sa, W, steps, warmup):
     """StreamingLLM decode: 128 sequences x 4096-slot cache, Hq=64, Hkv=8.
     Two cache copies alternate so no call finds the previous one's bytes in
@@ -211,7 +266,7 @@ def main():
         "roofline": roofline,
     }
     also = []
-    for fn in (bench_decode,):
+    for fn in (bench_streaming_prefill, bench_decode, bench_block_sparse):
         try:
             also.append(fn(torch, sa, W, args.steps, args.warmup))
         except Exception as e:  # noqa: BLE001 - report, keep the headline

@@ -1,0 +1,177 @@
+// dQ on gfx950 matrix cores (bfloat16, head_dim 128), query-major.
+//
+// dQ_i = alpha sum_j dS_ij K_j with dS = P (dO V^T - Delta) and P rebuilt
+// from L_new, which already holds the sink's e^{a_h} ("Attention Sink,
+// Learnable Sink and dsink" s8).  Computing dQ query-major, next to the
+// key-major dK/dV pass, replaces per-tile float32 atomics by one
+// deterministic store per element.
+//
+// Layout mirrors the forward: a wavefront owns 32 query rows of one head and
+// walks the same key-tile schedule.  S^T = K Q^T and dP^T = V dO^T come out
+// with one query per lane column, so L_new and Delta are per-lane scalars;
+// dS^T in bf16 is directly the B operand of dQ^T += K^T dS^T, whose K^T
+// operand comes from the staged K tile through ds_read_b64_tr_b16.
+#include "qmajor.cuh"
+
+namespace sa {
+namespace dq128 {
+
+using namespace qm;
+
+constexpr int NWQ = 8;      // wavefronts per workgroup (2 per SIMD)
+constexpr int QWQ = 32;     // query rows per wavefront
+
+__global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
+                                                    const uint16_t* __restrict__ Q,
+                                                    const uint16_t* __restrict__ K,
+                                                    const uint16_t* __restrict__ V,
+                                                    const uint16_t* __restrict__ dO, BwdWork w,
+                                                    uint16_t* __restrict__ dQ) {
+  __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];   // [stage][K, V]
+  __shared__ uint32_t bitmap[MAX_BITMAP_WORDS];
+
+  const WgCoord wc = wg_coord(geo, p.batch, blockIdx.x);
+  const int t0 = p.cu[wc.b];
+  const int L = p.cu[wc.b + 1] - t0;
+  const int p0 = wc.pt * geo.P;
+  if (p0 >= L) return;
+  const int p1 = min(L, p0 + geo.P);
+
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int gq = lane >> 5;
+  const int G = p.hq / p.hkv;
+  const int g = wc.g;
+  const int h = g * G + wc.hg * geo.hw + wv / geo.wph;
+  const int wq0 = p0 + (wv % geo.wph) * QWQ;
+  const int wq1 = min(L, wq0 + QWQ);
+  const int qoff = p.blocks ? q_block_offset(p.cu, wc.b) : 0;
+
+  // Q^T and dO^T as B operands (lane: query l32, dims gq*64 + ks*8), and the
+  // per-query L_new, Delta (rows past the sample: P = 0 through L_new = +inf).
+  const int qi = wq0 + l32;
+  bf16x8 qf[8], dof[8];
+  float Lq = kInf, Dq = 0.f;
+  if (qi < L) {
+    const size_t row = static_cast<size_t>(t0 + qi) * p.hq + h;
+    const uint16_t* qs = Q + row * D + gq * 64;
+    const uint16_t* ds = dO + row * D + gq * 64;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qs + ks * 8));
+      dof[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ds + ks * 8));
+    }
+    Lq = w.lnew[row];
+    Dq = w.delta[row];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      dof[ks] = qf[ks];
+    }
+  }
+  const float lb = Lq * kLog2e;
+
+  Sched sc = make_sched(p, L, qoff, g, p0, p1, bitmap);
+
+  const float c = p.scale * kLog2e;
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[dt][i] = 0.f;
+
+  const size_t kvs = static_cast<size_t>(p.hkv) * D;
+  const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
+  const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
+  auto issue = [&](int kt, int st) {
+    const int k0 = kt * BN;
+    const int nvalid = min(BN, L - k0);
+    load_tile_lds(Kg + static_cast<size_t>(k0) * kvs, kvs, nvalid, kv[st][0], wv, NWQ, lane);
+    load_tile_lds(Vg + static_cast<size_t>(k0) * kvs, kvs, nvalid, kv[st][1], wv, NWQ, lane);
+  };
+
+  int kt = sc.next();
+  if (kt >= 0) issue(kt, 0);
+  __syncthreads();
+  int stage = 0;
+  while (kt >= 0) {
+    const int kt_next = sc.next();
+    if (kt_next >= 0) issue(kt_next, stage ^ 1);
+
+    const int cls = wave_tile_class(p, qoff, g, wq0, wq1, kt);
+    if (cls != 0) {
+      const uint16_t* Ks = kv[stage][0];
+      const uint16_t* Vs = kv[stage][1];
+      const int k0 = kt * BN;
+      // S^T = K Q^T and dP^T = V dO^T : M = keys (2 tiles), N = 32 queries
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sacc[mt][i] = 0.f; pacc[mt][i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          sacc[mt] = mfma32(row_frag(Ks, mt * 32 + l32, gq * 8 + ks), qf[ks], sacc[mt]);
+          pacc[mt] = mfma32(row_frag(Vs, mt * 32 + l32, gq * 8 + ks), dof[ks], pacc[mt]);
+        }
+      }
+      // dS^T = P^T (dP^T - Delta); element i of lane (l32, gq) in M-tile mt is
+      // key k0 + 32mt + 8(i/4) + 4gq + i%4, query qi.
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c, -lb));
+          if (cls == 2) {
+            const int key = k0 + mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
+            if (!key_visible(qi, key, p.n_sink, p.window)) pe = 0.f;
+          }
+          pacc[mt][i] = pe * (pacc[mt][i] - Dq);
+        }
+      // dQ^T += K^T dS^T : M = dims (4 tiles), N = 32 queries, K = 64 keys.
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const bf16x8 dsb = pack_kstep(pacc[cc >> 1], cc & 1);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma32(tr_frag(Ks, 16 * cc, dt * 32, lane), dsb, dqacc[dt]);
+      }
+    }
+    __syncthreads();
+    stage ^= 1;
+    kt = kt_next;
+  }
+
+  // dQ = alpha * acc: lane (query qi, gq) holds dims dt*32 + 8u + 4gq + 0..3.
+  if (qi < wq1) {
+    uint16_t* dst = dQ + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + 4 * gq;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(p.scale * dqacc[dt][4 * u], p.scale * dqacc[dt][4 * u + 1]);
+        pk[1] = pack_bf16x2(p.scale * dqacc[dt][4 * u + 2], p.scale * dqacc[dt][4 * u + 3]);
+        *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * u) = pk;
+      }
+  }
+}
+
+}  // namespace dq128
+
+hipError_t launch_bwd_dq(const Prefill& p, const void* q, const void* k, const void* v,
+                         const void* dout, const BwdWork& w, void* dq, hipStream_t st) {
+  if (p.total == 0 || p.batch == 0) return hipSuccess;
+  const qm::Geo geo = qm::make_geo(p, dq128::NWQ, dq128::QWQ);
+  const long long grid = static_cast<long long>(geo.nptiles) * p.batch * geo.Z;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dq128::dq_kernel, dim3(static_cast<unsigned>(grid)), dim3(512), 0, st, p, geo,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), w,
+                     static_cast<uint16_t*>(dq));
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -55,8 +55,9 @@ hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* l
                                  bool zero_dkv, hipStream_t st);
 hipError_t launch_bwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
                               const void* dout, const BwdWork& w, void* dq, hipStream_t st);
+// Key-major dK/dV kernel followed by the query-major dQ kernel.
 hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
-                           const void* dout, const BwdWork& w, void* dk, void* dv,
+                           const void* dout, const BwdWork& w, void* dq, void* dk, void* dv,
                            hipStream_t st);
 bool bwd_mfma_supported(const Prefill& p);
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st);

@@ -1,0 +1,219 @@
+// Query-major machinery shared by the forward and the dQ kernels (bf16,
+// head_dim 128): workgroup geometry, the key-tile schedule of a group of
+// query rows, per-wavefront tile classification, direct-to-LDS tile loads and
+// the MFMA fragment readers.
+#pragma once
+
+#include "common.cuh"
+
+namespace sa {
+namespace qm {
+
+constexpr int D = 128;
+constexpr int BN = 64;                 // keys per tile (= block size of block lists)
+constexpr int NW = 4;                  // wavefronts per workgroup
+constexpr int QW = 64;                 // query rows per wavefront
+constexpr int TILE = BN * D;           // bf16 elements of one staged K or V tile (16 KB)
+constexpr int MAX_BITMAP_WORDS = 256;  // block lists: up to 8192 KV blocks per sample
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Geometry: a workgroup holds 4 wavefronts of one KV head g.  With G = Hq/Hkv
+// query heads per KV head, up to 4 of them share the workgroup (GQA packing:
+// each staged K/V tile feeds 4 x 64 query rows); with G = 2 or 1 the
+// wavefronts of a head take consecutive 64-row slabs.
+// ---------------------------------------------------------------------------
+struct Geo {
+  int hw;       // query heads per workgroup
+  int wph;      // wavefronts per head
+  int P;        // query positions per workgroup
+  int nptiles;  // position tiles per sample (from max_seqlen)
+  int nhg;      // head groups per KV head
+  int Z;        // hkv * nhg
+};
+
+// nw wavefronts of qw rows each (nw a power of two, qw dividing 64).
+inline Geo make_geo(const Prefill& p, int nw = NW, int qw = QW) {
+  Geo g;
+  const int G = p.hq / p.hkv;
+  g.hw = 1;
+  while (g.hw * 2 <= nw && G % (g.hw * 2) == 0) g.hw *= 2;
+  g.wph = nw / g.hw;
+  g.P = qw * g.wph;
+  g.nptiles = (p.max_seqlen + g.P - 1) / g.P;
+  g.nhg = G / g.hw;
+  g.Z = p.hkv * g.nhg;
+  return g;
+}
+
+// Flat block id -> coordinates: position tiles slowest and heaviest (latest)
+// first, then sample, then (KV head, head group).  Consecutive ids go to
+// different XCDs round-robin, so with Z a multiple of 8 every XCD serves fixed
+// KV heads and their K/V slices stay in that XCD's L2.
+struct WgCoord {
+  int pt, b, g, hg;
+};
+__device__ __forceinline__ WgCoord wg_coord(const Geo& geo, int batch, int bid) {
+  WgCoord c;
+  const int per_pt = batch * geo.Z;
+  c.pt = geo.nptiles - 1 - bid / per_pt;
+  const int rem = bid % per_pt;
+  c.b = rem / geo.Z;
+  const int z = rem % geo.Z;
+  c.g = z / geo.nhg;
+  c.hg = z % geo.nhg;
+  return c;
+}
+
+// The workgroup's key-tile schedule: ranges without block lists, else the
+// union bitmap of the selected blocks (built in LDS).
+struct Sched {
+  bool blk;
+  TileRanges tr;
+  int n;
+  int word, nwords;
+  uint32_t bits;
+  const uint32_t* bm;
+  __device__ __forceinline__ int next() {
+    if (!blk) return n < tr.count() ? tr.at(n++) : -1;
+    while (bits == 0) {
+      if (++word >= nwords) return -1;
+      bits = bm[word];
+    }
+    const int kb = word * 32 + __builtin_ctz(bits);
+    bits &= bits - 1;
+    return kb;
+  }
+};
+
+// Bitmap of the KV blocks selected by any query block in [p0, p1) (causal
+// blocks only).  Every thread of the workgroup must call it.
+__device__ __forceinline__ void build_block_bitmap(const Prefill& p, int L, int qoff, int g, int p0,
+                                                   int p1, uint32_t* bm, int* nwords_out) {
+  const int nkb = (L + BN - 1) / BN;
+  const int nwords = min((nkb + 31) / 32, MAX_BITMAP_WORDS);
+  for (int i = threadIdx.x; i < nwords; i += blockDim.x) bm[i] = 0u;
+  __syncthreads();
+  const int qb0 = p0 / BN, qb1 = (p1 - 1) / BN;
+  const int total = (qb1 - qb0 + 1) * p.max_blocks;
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int qb = qb0 + idx / p.max_blocks;
+    const int e = idx % p.max_blocks;
+    const int kb = p.blocks[(static_cast<size_t>(qoff + qb) * p.hkv + g) * p.max_blocks + e];
+    if (kb >= 0 && kb <= qb && (kb >> 5) < nwords) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+  }
+  __syncthreads();
+  *nwords_out = nwords;
+}
+
+__device__ __forceinline__ Sched make_sched(const Prefill& p, int L, int qoff, int g, int p0, int p1,
+                                            uint32_t* bitmap) {
+  Sched sc;
+  sc.blk = p.blocks != nullptr;
+  sc.n = 0;
+  sc.word = -1;
+  sc.bits = 0u;
+  sc.bm = bitmap;
+  sc.nwords = 0;
+  if (sc.blk) build_block_bitmap(p, L, qoff, g, p0, p1, bitmap, &sc.nwords);
+  else sc.tr = window_tiles(p0, p1, p.n_sink, p.window, BN);
+  return sc;
+}
+
+// Class of key tile kt for a wavefront's rows [wq0, wq1): 0 empty, 1 full,
+// 2 mixed.  With block lists the wavefront's own query block must select it.
+__device__ __forceinline__ int wave_tile_class(const Prefill& p, int qoff, int g, int wq0, int wq1,
+                                               int kt) {
+  if (wq0 >= wq1) return 0;
+  int cls = classify_tile(wq0, wq1, kt * BN, BN, p.n_sink, p.window);
+  if (cls != 0 && p.blocks != nullptr) {
+    const int32_t* row =
+        p.blocks + (static_cast<size_t>(qoff + wq0 / BN) * p.hkv + g) * p.max_blocks;
+    if (!row_selects(row, p.max_blocks, kt)) cls = 0;
+  }
+  return cls;
+}
+
+// ---------------------------------------------------------------------------
+// Staged tiles: 64 rows of 256 bytes, 16-byte chunks XOR-swizzled per row so
+// that (a) 8 consecutive rows at one logical chunk hit distinct banks (the
+// MFMA row-fragment reads) and (b) the 4 rows x 4 chunks of one transposed
+// read spread over distinct banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz16(int row) {
+  const int r = row & 15;
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+// Element offset of (row, logical chunk lc).
+__device__ __forceinline__ int at16(int row, int lc) { return row * D + ((lc ^ swz16(row)) << 3); }
+
+// Loads rows [r0, r0 + 64) of a [rows, stride] bf16 tensor into a staged tile
+// with global_load_lds_dwordx4: wavefront `wv` of `nw` issues 16/nw
+// instructions of 4 rows each.  Rows at or past `nvalid` read row nvalid - 1
+// (finite data; the caller masks them).
+__device__ __forceinline__ void load_tile_lds(const uint16_t* base, size_t row_stride, int nvalid,
+                                              uint16_t* lds_tile, int wv, int nw, int lane) {
+  const int per = 16 / nw;
+#pragma unroll 4
+  for (int j = 0; j < per; ++j) {
+    const int blk = wv * per + j;
+    const int row = 4 * blk + (lane >> 4);
+    const int src_row = min(row, nvalid - 1);
+    const int lc = (lane & 15) ^ swz16(row);
+    __builtin_amdgcn_global_load_lds(base + static_cast<size_t>(src_row) * row_stride + lc * 8,
+                                     lds_tile + 4 * blk * D, 16, 0, 0);
+  }
+}
+
+// 16-byte row fragment (8 consecutive dims of one row) of a staged tile.
+__device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int row, int lc) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + at16(row, lc)));
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr(const uint16_t* lds_ptr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<uint16_t*>(lds_ptr)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Transposed 32x32x16 operand fragment of a staged tile: lane (column
+// 16*(grp%2) + i of a 32-wide dim block starting at dim0, k-half grp/2) gets
+// dims dim0 + 16*(grp%2) + i of rows rbase + 4*(grp/2) + {0..3} and
+// rbase + 8 + 4*(grp/2) + {0..3}.  With ds_read_b64_tr_b16, source lane
+// 4r + q of each 16-lane group reads 4 dims of row r, and the hardware hands
+// lane i the value of dim i in each of the 4 rows.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int rbase, int dim0, int lane) {
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int r = l16 >> 2, q4 = l16 & 3;
+  const int d = dim0 + 16 * (grp & 1) + 4 * q4;
+  const int lc = d >> 3, off = d & 7;
+  const int ra = rbase + 4 * (grp >> 1) + r;
+  const int rb = ra + 8;
+  const u32x2 a = ds_read_tr(tile + at16(ra, lc) + off);
+  const u32x2 b = ds_read_tr(tile + at16(rb, lc) + off);
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// k-step cc (16 keys) of a 64-key contraction as a B (or A) operand from two
+// 32x32 result tiles: elements (cc%2)*8 .. +8 of tile cc/2.  Logical k slot t
+// of lane half gq is key 16cc + 8(t/4) + 4gq + t%4, which matches tr_frag
+// with rbase = 16cc.
+__device__ __forceinline__ bf16x8 pack_kstep(const f32x16& t, int half) {
+  u32x4 u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(t[half * 8 + 2 * e], t[half * 8 + 2 * e + 1]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+}  // namespace qm
+}  // namespace sa

@@ -107,9 +107,9 @@ BwdLayout bwd_layout(const sa::Prefill& p) {
   l.delta = off; off += round_up(rows * 4);
   l.lnew = off; off += round_up(rows * 4);
   l.terms = off; off += round_up(rows * 4);
-  l.dq_acc = off; off += mfma ? round_up(rows * p.d * 4) : 0;
-  l.dk_acc = off; off += round_up(kv * 4);
-  l.dv_acc = off; off += round_up(kv * 4);
+  l.dq_acc = off;                                   // unused: dQ is stored directly
+  l.dk_acc = off; off += mfma ? 0 : round_up(kv * 4);
+  l.dv_acc = off; off += mfma ? 0 : round_up(kv * 4);
   const size_t nl = p.blocks ? static_cast<size_t>(p.nqb) * p.hkv : 0;
   l.csr_off = off; off += (p.blocks && mfma) ? round_up((nl + 1) * 4) : 0;
   l.csr_idx = off; off += (p.blocks && mfma) ? round_up(nl * p.max_blocks * 4) : 0;
@@ -331,10 +331,10 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     const bool mfma = sa::bwd_mfma_supported(p);
     hipError_t e;
     if (mfma) {
-      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dq=*/true, /*zero_dkv=*/true, st);
+      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dq=*/false, /*zero_dkv=*/false, st);
       if (e == hipSuccess && p.blocks != nullptr) e = sa::launch_block_csr(p, w, st);
-      if (e == hipSuccess) e = sa::launch_bwd_mfma(p, q, k, v, dout, w, dk, dv, st);
-      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dq, dk, dv, true, false, st);
+      if (e == hipSuccess) e = sa::launch_bwd_mfma(p, q, k, v, dout, w, dq, dk, dv, st);
+      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dq, dk, dv, false, false, st);
     } else {
       e = sa::launch_bwd_preprocess(p, o, lse, dout, w, false, true, st);
       if (e == hipSuccess) e = sa::launch_bwd_generic(p, q, k, v, dout, w, dq, st);
