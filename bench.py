@@ -232,6 +232,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", choices=("all", "headline", "decode"), default="all",
+                    help="headline: only the GQA prefill forward (for profiler runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one 1 GiB device-to-device copy (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
@@ -243,6 +248,16 @@ def main():
     from streamingllm_sink_attn_amd import workloads as W
 
     sa.lib()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+    if args.legs == "decode":
+        print(json.dumps(bench_decode(torch, sa, W, args.steps, args.warmup)), flush=True)
+        return
     head = bench_gqa_prefill(torch, sa, W, args.steps, args.warmup)
     wl = head.pop("wl")
     roofline = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
@@ -266,13 +281,15 @@ def main():
         "roofline": roofline,
     }
     also = []
-    for fn in (bench_streaming_prefill, bench_decode, bench_block_sparse):
+    legs = (bench_streaming_prefill, bench_decode, bench_block_sparse) if args.legs == "all" else ()
+    for fn in legs:
         try:
             also.append(fn(torch, sa, W, args.steps, args.warmup))
         except Exception as e:  # noqa: BLE001 - report, keep the headline
             also.append({"workload": fn.__name__, "error": repr(e)})
         torch.cuda.empty_cache()
-    line["also"] = also
+    if also:
+        line["also"] = also
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(line), flush=True)

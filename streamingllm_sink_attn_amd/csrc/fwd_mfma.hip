@@ -6,22 +6,32 @@
 // s = sigma(L_orig - a_h) and O_new = s O_orig (s4).  lse is L_orig.
 //
 // Work decomposition (geometry and schedule in qmajor.cuh):
-//   * A workgroup is 4 wavefronts of one KV head; each wavefront owns 64
-//     query rows of one query head.  Keys come in 64-key tiles loaded straight
-//     into LDS (global_load_lds_dwordx4, double-buffered), and only the tiles
-//     the mask can reach are visited: every causal tile, or the first-token
-//     tiles plus the window tiles, or the union of the selected blocks.  Each
-//     wavefront classifies a tile as empty (skipped), full, or mixed (element
-//     mask).
+//   * A workgroup is 8 wavefronts (2 per SIMD) of one KV head; each
+//     wavefront owns 32 query rows of one query head.  Keys come in 64-key
+//     tiles loaded straight into LDS (global_load_lds_dwordx4), and only the
+//     tiles the mask can reach are visited: every causal tile, or the
+//     first-token tiles plus the window tiles, or the union of the selected
+//     blocks.  Each wavefront classifies a tile as empty (skipped), full, or
+//     mixed (element mask).
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 result each lane holds 16 keys
 //     of ONE query (its column), so the online-softmax max and sum stay in
-//     registers plus one exchange between the two lane halves.  The same
+//     registers plus one v_permlane32_swap between the lane halves.  The same
 //     registers, converted to bf16, are the B operand of O^T += V^T P^T; the
 //     V^T operand comes from the staged V tile by ds_read_b64_tr_b16.
+//   * Software pipeline: the scores of tile j+1 are computed in the same
+//     basic block as the exponentials of tile j, and O += V P of tile j next
+//     to the mask and max of tile j+1, so the matrix core and the vector ALU
+//     work at the same time.  K runs one tile ahead of V: K and V each have
+//     two LDS buffers.
 //   * Online softmax with lazy rescaling: the exponent base only moves when a
 //     row's max grows by more than 2^8 (P <= 256), which is exact because O
 //     and l always share the same base.
+//   * LDS addresses: the per-lane swizzled offsets are computed once; the
+//     loop is unrolled by two so buffer offsets are instruction immediates.
+#include <cstdlib>
+#include <type_traits>
+
 #include "qmajor.cuh"
 
 namespace sa {
@@ -30,15 +40,37 @@ namespace fwd128 {
 using namespace qm;
 
 constexpr float kRescaleLog2 = 8.f;    // lazy-rescale threshold (log2 units)
+constexpr int FNW = 8;                 // wavefronts per workgroup
+constexpr int FQW = 32;                // query rows per wavefront
 
-__global__ __launch_bounds__(256, 1) void fwd_kernel(Prefill p, Geo geo,
-                                                     const uint16_t* __restrict__ Q,
-                                                     const uint16_t* __restrict__ K,
-                                                     const uint16_t* __restrict__ V,
-                                                     uint16_t* __restrict__ O,
-                                                     float* __restrict__ lse_out,
-                                                     float* __restrict__ s_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];   // [stage][K, V]
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const lds_char* base, int byte_off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + byte_off));
+}
+__device__ __forceinline__ u32x2 lds_tr(const lds_char* base, int byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) i16x4*)(base + byte_off)));
+}
+
+__global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
+                                                          const uint16_t* __restrict__ Q,
+                                                          const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V,
+                                                          uint16_t* __restrict__ O,
+                                                          float* __restrict__ lse_out,
+                                                          float* __restrict__ s_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][TILE];
   __shared__ uint32_t bitmap[MAX_BITMAP_WORDS];
 
   const WgCoord wc = wg_coord(geo, p.batch, blockIdx.x);
@@ -56,25 +88,42 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(Prefill p, Geo geo,
   const int G = p.hq / p.hkv;
   const int g = wc.g;
   const int h = g * G + wc.hg * geo.hw + w / geo.wph;
-  const int wq0 = p0 + (w % geo.wph) * QW;
-  const int wq1 = min(L, wq0 + QW);
-  const bool wave_rows = wq0 < wq1;
+  const int wq0 = p0 + (w % geo.wph) * FQW;
+  const int wq1 = min(L, wq0 + FQW);
+  const int qi = wq0 + l32;                          // this lane's query row
   const int qoff = p.blocks ? q_block_offset(p.cu, wc.b) : 0;
 
-  // Q^T as the B operand: lane (query l32 of N-tile nt, half gq) holds dims
-  // gq*64 + ks*8 .. +8 for k-step ks (the K fragments use the same order).
-  bf16x8 qf[2][8];
+  // Q^T as the B operand: lane (query l32, half gq) holds dims gq*64 + ks*8
+  // .. +8 for k-step ks (the K fragments use the same order).
+  bf16x8 qf[8];
+  if (qi < L) {
+    const uint16_t* src = Q + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + gq * 64;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int qi = wq0 + nt * 32 + l32;
-    if (qi < L) {
-      const uint16_t* src = Q + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + gq * 64;
+    for (int ks = 0; ks < 8; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 8));
+  } else {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        qf[nt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 8));
-    } else {
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // Per-lane swizzled LDS byte offsets (tile rows are 256 bytes).
+  //   K fragment (mt, ks): row mt*32 + l32, logical chunk gq*8 + ks.
+  //   V^T fragment (cc, dt): rows 16cc + ra0 and 16cc + ra0 + 8, logical
+  //   chunk dt*4 + c4, byte 2*(d & 7) inside it (see tr_frag in qmajor.cuh).
+  int koff[8], voa[4], vob[4];
+  {
+    const int sk = swz16(l32);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int ks = 0; ks < 8; ++ks) koff[ks] = l32 * 256 + (((gq * 8 + ks) ^ sk) << 4);
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int ra0 = 4 * (grp >> 1) + (l16 >> 2);
+    const int d4 = 16 * (grp & 1) + 4 * (l16 & 3);           // dim offset inside the 32-dim block
+    const int c4 = d4 >> 3, off = (d4 & 7) * 2;
+    const int sa_ = swz16(ra0), sb_ = swz16(ra0 + 8);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      voa[dt] = ra0 * 256 + (((dt * 4 + c4) ^ sa_) << 4) + off;
+      vob[dt] = (ra0 + 8) * 256 + (((dt * 4 + c4) ^ sb_) << 4) + off;
     }
   }
 
@@ -82,163 +131,201 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(Prefill p, Geo geo,
 
   const float c = p.scale * kLog2e;                  // exp(scale*x) = exp2(c*x)
   const float thr = kRescaleLog2 / c;                // raw-score rescale threshold
-  f32x16 oacc[4][2];
+  f32x16 oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][nt][i] = 0.f;
-  float mrun[2] = {-kInf, -kInf};
-  float lsum[2] = {0.f, 0.f};
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float mrun = -kInf, lsum = 0.f;
 
   const size_t kvs = static_cast<size_t>(p.hkv) * D;
   const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
   const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
-  auto issue = [&](int kt, int st) {
+  auto issue_k = [&](int kt, int st) {
     const int k0 = kt * BN;
-    const int nvalid = min(BN, L - k0);
-    load_tile_lds(Kg + static_cast<size_t>(k0) * kvs, kvs, nvalid, kv[st][0], w, NW, lane);
-    load_tile_lds(Vg + static_cast<size_t>(k0) * kvs, kvs, nvalid, kv[st][1], w, NW, lane);
+    load_tile_lds(Kg + static_cast<size_t>(k0) * kvs, kvs, min(BN, L - k0), kbuf[st], w, FNW, lane);
   };
+  auto issue_v = [&](int kt, int st) {
+    const int k0 = kt * BN;
+    load_tile_lds(Vg + static_cast<size_t>(k0) * kvs, kvs, min(BN, L - k0), vbuf[st], w, FNW, lane);
+  };
+  auto tile_class = [&](int kt) { return kt >= 0 ? wave_tile_class(p, qoff, g, wq0, wq1, kt) : 0; };
 
-  int kt = sc.next();
-  if (kt >= 0) issue(kt, 0);
-  __syncthreads();
-  int stage = 0;
-  while (kt >= 0) {
-    const int kt_next = sc.next();
-    if (kt_next >= 0) issue(kt_next, stage ^ 1);
-
-    const int cls = wave_tile_class(p, qoff, g, wq0, wq1, kt);
-    if (cls != 0) {
-      const uint16_t* Ks = kv[stage][0];
-      const uint16_t* Vs = kv[stage][1];
-      const int k0 = kt * BN;
-      // S^T = K Q^T : M = keys (2 tiles of 32), N = queries (2 tiles), K = 128
-      f32x16 sacc[2][2];
+  // S^T of a tile from K buffer ST.
+  auto scores = [&](auto ST, f32x16 (&s)[2]) {
+    const lds_char* kb = (const lds_char*)(kbuf[decltype(ST)::value]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+      for (int i = 0; i < 16; ++i) s[mt][i] = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[mt][nt][i] = 0.f;
+      for (int ks = 0; ks < 8; ++ks) s[mt] = mfma32(lds_frag(kb, koff[ks] + mt * 8192), qf[ks], s[mt]);
+    }
+  };
+  // Element mask of a mixed tile: element i of M-tile mt is key
+  // k0 + 32mt + 8(i/4) + 4gq + i%4.
+  auto mask = [&](int kt, f32x16 (&s)[2]) {
+    const int k0 = kt * BN;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 kf = row_frag(Ks, mt * 32 + l32, gq * 8 + ks);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][ks], sacc[mt][nt]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
+        if (!key_visible(qi, key, p.n_sink, p.window)) s[mt][i] = -kInf;
       }
-      // Element mask on mixed tiles.  Result element i of lane (l32, gq) in
-      // M-tile mt is key 8*(i/4) + 4*gq + i%4 of that M-tile, query l32.
-      if (cls == 2) {
+  };
+  // Row max of a tile and the lazy rescale to a new base of O, l and the
+  // not yet accumulated probabilities pend (which share the old base).
+  auto update_max = [&](const f32x16 (&s)[2], bf16x8 (&pend)[4]) {
+    float m0 = -kInf;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int qi = wq0 + nt * 32 + l32;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) m0 = __builtin_fmaxf(m0, s[mt][i]);
+    m0 = xhalf_max(m0);
+    if (__ballot(m0 > mrun + thr) != 0) {
+      const float mnew = __builtin_fmaxf(mrun, m0);
+      const float f = (mrun == -kInf) ? 0.f : __builtin_amdgcn_exp2f((mrun - mnew) * c);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
-              if (!key_visible(qi, key, p.n_sink, p.window)) sacc[mt][nt][i] = -kInf;
-            }
-        }
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        u32x4 u = __builtin_bit_cast(u32x4, pend[cc]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          u[e] = pack_bf16x2(__uint_as_float(u[e] << 16) * f, __uint_as_float(u[e] & 0xffff0000u) * f);
+        pend[cc] = __builtin_bit_cast(bf16x8, u);
       }
-      // Online softmax (per lane = per query column).
-      float mx[2];
+      lsum *= f;
+      mrun = mnew;
+    }
+  };
+  // P = 2^(c x - c m) in bf16 as four k-steps, l += sum P.
+  auto probs = [&](f32x16 (&s)[2], bf16x8 (&pf)[4]) {
+    const float mb = (mrun == -kInf) ? 0.f : mrun * c;
+    float ls = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float m0 = -kInf;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, sacc[mt][nt][i]);
-        mx[nt] = fmaxf(m0, __shfl_xor(m0, 32));
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], c, -mb));
+        s[mt][i] = e;
+        ls += e;
       }
-      const bool need = (mx[0] > mrun[0] + thr) || (mx[1] > mrun[1] + thr);
-      if (__ballot(need) != 0) {
+    lsum += ls;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const float mnew = fmaxf(mrun[nt], mx[nt]);
-          const float f = (mrun[nt] == -kInf) ? 0.f : __builtin_amdgcn_exp2f((mrun[nt] - mnew) * c);
+    for (int cc = 0; cc < 4; ++cc) pf[cc] = pack_kstep(s[cc >> 1], cc & 1);
+  };
+  // O^T += V^T P^T from V buffer ST.
+  auto pv = [&](auto ST, const bf16x8 (&pf)[4]) {
+    const lds_char* vb = (const lds_char*)(vbuf[decltype(ST)::value]);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][nt][i] *= f;
-          lsum[nt] *= f;
-          mrun[nt] = mnew;
-        }
-      }
-      bf16x8 pf[2][4];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float mb = (mrun[nt] == -kInf) ? 0.f : mrun[nt] * c;
-        float ls = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][nt][i], c, -mb));
-            sacc[mt][nt][i] = e;
-            ls += e;
-          }
-        lsum[nt] += ls;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) pf[nt][cc] = pack_kstep(sacc[cc >> 1][nt], cc & 1);
-      }
-      // O^T += V^T P^T : M = dims (4 tiles), N = queries (2), K = 64 keys (4 steps).
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16x8 vf = tr_frag(Vs, 16 * cc, dt * 32, lane);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) oacc[dt][nt] = mfma32(vf, pf[nt][cc], oacc[dt][nt]);
-        }
+        const u32x2 a = lds_tr(vb, voa[dt] + cc * 4096);
+        const u32x2 b = lds_tr(vb, vob[dt] + cc * 4096);
+        oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]}), pf[cc], oacc[dt]);
       }
+  };
+
+  // A tile this wavefront does not see gets scores of -inf: its P is 0 and
+  // it changes nothing, so the steady state needs no per-wavefront branch.
+  auto kill = [&](f32x16 (&s)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[mt][i] = -kInf;
+  };
+  // Mask (or kill) the scores of tile kt and move the base if needed.
+  auto finish_scores = [&](int kt, f32x16 (&s)[2], bf16x8 (&pend)[4]) {
+    const int cls = tile_class(kt);
+    if (cls == 0) kill(s);
+    else if (cls == 2) mask(kt, s);
+    update_max(s, pend);
+  };
+
+  int t_cur = sc.next();
+  if (t_cur >= 0) {
+    int t_nx = sc.next();
+    issue_k(t_cur, 0);
+    issue_v(t_cur, 0);
+    if (t_nx >= 0) issue_k(t_nx, 1);
+    __syncthreads();
+    bf16x8 pf[4];                                    // P of tile "cur" (bf16)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pf[cc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    {
+      f32x16 s0[2];
+      scores(std::integral_constant<int, 0>{}, s0);
+      finish_scores(t_cur, s0, pf);
+      probs(s0, pf);
     }
     __syncthreads();
-    stage ^= 1;
-    kt = kt_next;
+
+    // One pipeline step: P of tile "cur" is in pf and its V in V buffer ST;
+    // K of tile "nx" is in K buffer ST^1.  K of the tile after next goes to K
+    // buffer ST and V of "nx" to V buffer ST^1.  O += V P of "cur" (matrix
+    // core) is interleaved with the exponentials of "nx" (vector ALU).
+    auto step = [&](auto ST) {
+      constexpr int st = decltype(ST)::value;
+      const int t_nx2 = sc.next();
+      if (t_nx2 >= 0) issue_k(t_nx2, st);
+      if (t_nx >= 0) {                               // uniform over the workgroup
+        issue_v(t_nx, st ^ 1);
+        f32x16 s_nx[2];
+        scores(std::integral_constant<int, st ^ 1>{}, s_nx);
+        finish_scores(t_nx, s_nx, pf);
+        bf16x8 pn[4];
+        pv(std::integral_constant<int, st>{}, pf);
+        probs(s_nx, pn);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) pf[cc] = pn[cc];
+      } else {
+        pv(std::integral_constant<int, st>{}, pf);
+      }
+      __syncthreads();
+      t_cur = t_nx;
+      t_nx = t_nx2;
+    };
+    while (true) {
+      step(std::integral_constant<int, 0>{});
+      if (t_cur < 0) break;
+      step(std::integral_constant<int, 1>{});
+      if (t_cur < 0) break;
+    }
   }
 
   // Epilogue: L_orig = alpha*m + ln l; s = sigma(L_orig - a_h); O = acc * s / l.
-  if (!wave_rows) return;
+  const float lt = xhalf_sum(lsum);
+  if (qi >= wq1) return;
   const bool has_sink = p.sink != nullptr;
-  const float a = has_sink ? p.sink[h] : 0.f;
+  float L_orig, s_val, mul;
+  if (lt > 0.f) {
+    L_orig = mrun * p.scale + __logf(lt);
+    s_val = has_sink ? 1.f / (1.f + __expf(p.sink[h] - L_orig)) : 1.f;
+    mul = s_val / lt;
+  } else {
+    L_orig = -kInf;
+    s_val = has_sink ? 0.f : 1.f;
+    mul = 0.f;
+  }
+  uint16_t* dst = O + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + 4 * gq;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const float lt = lsum[nt] + __shfl_xor(lsum[nt], 32);
-    const int qi = wq0 + nt * 32 + l32;
-    if (qi >= wq1) continue;
-    float L_orig, s_val, mul;
-    if (lt > 0.f) {
-      L_orig = mrun[nt] * p.scale + __logf(lt);
-      s_val = has_sink ? 1.f / (1.f + __expf(a - L_orig)) : 1.f;
-      mul = s_val / lt;
-    } else {
-      L_orig = -kInf;
-      s_val = has_sink ? 0.f : 1.f;
-      mul = 0.f;
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(oacc[dt][4 * u] * mul, oacc[dt][4 * u + 1] * mul);
+      pk[1] = pack_bf16x2(oacc[dt][4 * u + 2] * mul, oacc[dt][4 * u + 3] * mul);
+      *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * u) = pk;
     }
-    uint16_t* dst = O + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + 4 * gq;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(oacc[dt][nt][4 * u] * mul, oacc[dt][nt][4 * u + 1] * mul);
-        pk[1] = pack_bf16x2(oacc[dt][nt][4 * u + 2] * mul, oacc[dt][nt][4 * u + 3] * mul);
-        *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * u) = pk;
-      }
-    if (gq == 0) {
-      const size_t r = static_cast<size_t>(t0 + qi) * p.hq + h;
-      lse_out[r] = L_orig;
-      if (s_out) s_out[r] = s_val;
-    }
+  if (gq == 0) {
+    const size_t r = static_cast<size_t>(t0 + qi) * p.hq + h;
+    lse_out[r] = L_orig;
+    if (s_out) s_out[r] = s_val;
   }
 }
 
@@ -262,14 +349,14 @@ __global__ __launch_bounds__(256) void visit_map_kernel(Prefill p, Geo geo, uint
   }
   uint8_t* m = out + base + static_cast<size_t>(wc.g) * L * L;
   Sched sc = make_sched(p, L, qoff, wc.g, p0, p1, bitmap);
-  // The wavefronts of the first head of the workgroup: each covers QW rows.
+  // The wavefronts of the first head of the workgroup: each covers FQW rows.
   for (int kt = sc.next(); kt >= 0; kt = sc.next()) {
     for (int wv = 0; wv < geo.wph; ++wv) {
-      const int wq0 = p0 + wv * QW;
-      const int wq1 = min(L, wq0 + QW);
+      const int wq0 = p0 + wv * FQW;
+      const int wq1 = min(L, wq0 + FQW);
       const int cls = wave_tile_class(p, qoff, wc.g, wq0, wq1, kt);
       if (cls == 0) continue;
-      for (int e = threadIdx.x; e < QW * BN; e += blockDim.x) {
+      for (int e = threadIdx.x; e < FQW * BN; e += blockDim.x) {
         const int qi = wq0 + e / BN;
         const int key = kt * BN + e % BN;
         if (qi >= wq1 || key >= L) continue;
@@ -291,18 +378,18 @@ bool fwd_mfma_supported(const Prefill& p) {
 hipError_t launch_fwd_mfma(const Prefill& p, const void* q, const void* k, const void* v, void* o,
                            float* lse, float* s, hipStream_t st) {
   if (p.total == 0 || p.batch == 0) return hipSuccess;
-  const qm::Geo geo = qm::make_geo(p);
+  const qm::Geo geo = qm::make_geo(p, fwd128::FNW, fwd128::FQW);
   const long long grid = static_cast<long long>(geo.nptiles) * p.batch * geo.Z;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd128::fwd_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, p, geo,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  hipLaunchKernelGGL(fwd128::fwd_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * fwd128::FNW), 0,
+                     st, p, geo, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, s);
   return hipGetLastError();
 }
 
 hipError_t launch_visit_map(const Prefill& p, uint8_t* out, hipStream_t st) {
   if (p.total == 0 || p.batch == 0) return hipSuccess;
-  const qm::Geo geo = qm::make_geo(p);
+  const qm::Geo geo = qm::make_geo(p, fwd128::FNW, fwd128::FQW);
   const long long grid = static_cast<long long>(geo.nptiles) * p.batch * geo.Z;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(fwd128::visit_map_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,

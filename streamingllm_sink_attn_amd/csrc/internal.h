@@ -7,7 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/sink_attn.h"
+#include "sink_attn.h"
 
 namespace sa {
 
