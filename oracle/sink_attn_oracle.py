@@ -301,22 +301,41 @@ def _row_keys(cu, qoff, t, g, n_sink, window, block_indices, block_size):
 
 
 def _row_state(q, k, v, cu, qoff, t, h, scale, n_sink, window, block_indices, block_size, a):
+    """The forward quantities of query row (t, h), in float64 (only the rows
+    read are converted)."""
     hq, hkv = q.shape[1], k.shape[1]
     g = kv_head(h, hq, hkv)
     keys, _ = _row_keys(cu, qoff, t, g, n_sink, window, block_indices, block_size)
-    x = scale * (k[keys, g, :] @ q[t, h, :])
+    kk = np.asarray(k[keys, g, :], dtype=np.float64)
+    x = scale * (kk @ np.asarray(q[t, h, :], dtype=np.float64))
     lorig = logsumexp_rows(x[None, :])[0]
-    lnew, s, _ = _sink_terms(np.array([lorig]), None if a is None else a[h])
+    lnew, s, _ = _sink_terms(np.array([lorig]), None if a is None else float(a[h]))
     lnew, s = lnew[0], s[0]
     p = np.exp(x - lnew) if np.isfinite(lnew) else np.zeros(len(keys))
-    o = p @ v[keys, g, :]
+    o = p @ np.asarray(v[keys, g, :], dtype=np.float64)
     return keys, g, p, o, lorig, s
+
+
+def _pair_visible(cu, qoff, t, tj, g, n_sink, window, block_indices, block_size):
+    """Whether key token tj is valid for query token t and KV head g (the
+    same definition as sample_mask, for one pair)."""
+    b = int(np.searchsorted(cu, t, side="right") - 1)
+    if not (cu[b] <= tj <= t):
+        return False
+    i, j = t - int(cu[b]), tj - int(cu[b])
+    if window > 0 and not (j < n_sink or i - j < window):
+        return False
+    if block_indices is not None:
+        row = np.asarray(block_indices[qoff[b] + i // block_size, g])
+        if not np.any(row == j // block_size):
+            return False
+    return True
 
 
 def fwd_rows(q, k, v, cu_seqlens, scale, rows, n_sink=0, window=0, block_indices=None,
              block_size=64, sink=None):
     """Forward for the given (token, head) pairs only: (O [n,D], lse [n], s [n])."""
-    q, k, v, a = _as64(q), _as64(k), _as64(v), _as64(sink)
+    a = _as64(sink)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     qoff = _q_block_offsets(cu, block_size)
     outs, lses, ss = [], [], []
@@ -335,7 +354,7 @@ def bwd_rows(q, k, v, cu_seqlens, scale, do, rows, n_sink=0, window=0, block_ind
 
     Returns (dQ [n,D], delta [n], one_minus_s [n]).
     """
-    q, k, v, do, a = _as64(q), _as64(k), _as64(v), _as64(do), _as64(sink)
+    a = _as64(sink)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     qoff = _q_block_offsets(cu, block_size)
     dqs, deltas, oms = [], [], []
@@ -343,10 +362,11 @@ def bwd_rows(q, k, v, cu_seqlens, scale, do, rows, n_sink=0, window=0, block_ind
         t, h = int(t), int(h)
         keys, g, p, o, _, s = _row_state(q, k, v, cu, qoff, t, h, scale,
                                          n_sink, window, block_indices, block_size, a)
-        delta = float(do[t, h] @ o)
-        dp = v[keys, g, :] @ do[t, h]
+        dot = np.asarray(do[t, h], dtype=np.float64)
+        delta = float(dot @ o)
+        dp = np.asarray(v[keys, g, :], dtype=np.float64) @ dot
         ds = p * (dp - delta)
-        dqs.append(scale * (ds @ k[keys, g, :]))
+        dqs.append(scale * (ds @ np.asarray(k[keys, g, :], dtype=np.float64)))
         deltas.append(delta)
         oms.append(1.0 - s)
     return np.array(dqs), np.array(deltas), np.array(oms)
@@ -359,7 +379,7 @@ def bwd_kv_rows(q, k, v, cu_seqlens, scale, do, kv_rows, n_sink=0, window=0,
     Each is a sum over every (query row, query head of the group) that sees
     the key; every such query row is evaluated in full.
     """
-    q, k, v, do, a = _as64(q), _as64(k), _as64(v), _as64(do), _as64(sink)
+    a = _as64(sink)
     hq, hkv = q.shape[1], k.shape[1]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     qoff = _q_block_offsets(cu, block_size)
@@ -374,17 +394,17 @@ def bwd_kv_rows(q, k, v, cu_seqlens, scale, do, kv_rows, n_sink=0, window=0,
             if kv_head(h, hq, hkv) != g:
                 continue
             for t in range(tj, t1):
+                if not _pair_visible(cu, qoff, t, tj, g, n_sink, window, block_indices, block_size):
+                    continue
                 keys, _, p, o, _, _ = _row_state(q, k, v, cu, qoff, t, h, scale,
                                                  n_sink, window, block_indices, block_size, a)
-                hit = np.nonzero(keys == tj)[0]
-                if len(hit) == 0:
-                    continue
-                pj = p[hit[0]]
-                delta = float(do[t, h] @ o)
-                dpj = float(v[tj, g] @ do[t, h])
+                pj = p[np.nonzero(keys == tj)[0][0]]
+                dot = np.asarray(do[t, h], dtype=np.float64)
+                delta = float(dot @ o)
+                dpj = float(np.asarray(v[tj, g], dtype=np.float64) @ dot)
                 dsj = pj * (dpj - delta)
-                dk_row += scale * dsj * q[t, h]
-                dv_row += pj * do[t, h]
+                dk_row += scale * dsj * np.asarray(q[t, h], dtype=np.float64)
+                dv_row += pj * dot
         dks.append(dk_row)
         dvs.append(dv_row)
     return np.array(dks), np.array(dvs)

@@ -47,22 +47,24 @@ inline Geo make_geo(const Prefill& p, int nw = NW, int qw = QW) {
   return g;
 }
 
-// Flat block id -> coordinates: position tiles slowest and heaviest (latest)
-// first, then sample, then (KV head, head group).  Consecutive ids go to
-// different XCDs round-robin, so with Z a multiple of 8 every XCD serves fixed
-// KV heads and their K/V slices stay in that XCD's L2.
+// Flat block id -> coordinates: sample slowest, then position tiles heaviest
+// (latest) first, then (KV head, head group) fastest.  Consecutive ids go to
+// the XCDs round-robin, so with Z a multiple of 8 every XCD serves fixed KV
+// heads, and working one sample at a time keeps that sample's K/V slice of
+// each KV head resident in the XCD's L2.
 struct WgCoord {
   int pt, b, g, hg;
 };
 __device__ __forceinline__ WgCoord wg_coord(const Geo& geo, int batch, int bid) {
   WgCoord c;
-  const int per_pt = batch * geo.Z;
-  c.pt = geo.nptiles - 1 - bid / per_pt;
-  const int rem = bid % per_pt;
-  c.b = rem / geo.Z;
+  const int per_b = geo.nptiles * geo.Z;
+  c.b = bid / per_b;
+  const int rem = bid % per_b;
+  c.pt = geo.nptiles - 1 - rem / geo.Z;
   const int z = rem % geo.Z;
   c.g = z / geo.nhg;
   c.hg = z % geo.nhg;
+  (void)batch;
   return c;
 }
 
