@@ -232,7 +232,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", choices=("all", "headline", "decode"), default="all",
+    ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks"),
+                    default="all",
                     help="headline: only the GQA prefill forward (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (a kernel of known "
@@ -255,8 +256,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    if args.legs == "decode":
-        print(json.dumps(bench_decode(torch, sa, W, args.steps, args.warmup)), flush=True)
+    single = {"decode": bench_decode, "streaming": bench_streaming_prefill,
+              "blocks": bench_block_sparse}
+    if args.legs in single:
+        print(json.dumps(single[args.legs](torch, sa, W, args.steps, args.warmup)), flush=True)
         return
     head = bench_gqa_prefill(torch, sa, W, args.steps, args.warmup)
     wl = head.pop("wl")

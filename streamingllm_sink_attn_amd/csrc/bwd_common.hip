@@ -191,6 +191,12 @@ __global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* off, int n) {
   if (tid == 0) off[0] = 0;
 }
 
+hipError_t launch_scan(int32_t* off, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, st, off, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st) {
   const int n = p.nqb * p.hkv;
   if (n == 0) return hipSuccess;

@@ -9,18 +9,31 @@
 // adds it again (s10's double-count warning).
 //
 // Work decomposition:
-//   * One workgroup of 2 wavefronts owns a 64-key tile of one KV head (one
-//     block of the block lists); wavefront w owns keys 32w..32w+31.  It walks
-//     every (query head of the group, 64-row query tile) that can see the
-//     tile: the causal tiles, the window tiles (every tile for a tile holding
-//     first tokens), or the reverse block list of the tile.  dK and dV stay in
-//     registers across all of them and are written once.
-//   * Per (head, query tile): S = Q K^T and dP = dO V^T with
+//   * A key tile is 64 keys of one KV head (one block of the block lists).
+//     Its iterations are the (query head of the group, 64-row query tile)
+//     pairs that can see it: the causal tiles, the window tiles (every tile
+//     for a tile holding first tokens), or the reverse block list of the tile
+//     ("Attention Sink, Learnable Sink and dsink" s10: work split by KV-block
+//     reverse lists).
+//   * Tiles differ a lot in work (a first-token tile, or block 0 that every
+//     block list selects, is seen by every query tile), so a planning kernel
+//     cuts every tile's iterations into chunks of at most kChunk and a
+//     persistent kernel pulls chunks from work queues (one per XCD, keyed by
+//     KV head, so one XCD's L2 streams one head group's Q/dO).  A tile done in
+//     one chunk writes bf16 dK/dV directly; a split tile adds its chunks'
+//     float32 partials atomically (once per chunk) and a convert kernel
+//     finishes it.
+//   * A chunk runs on a workgroup of 2 wavefronts, wavefront w owning keys
+//     32w..32w+31.  Per iteration: S = Q K^T and dP = dO V^T with
 //     v_mfma_f32_32x32x16_bf16 (lane column = key), so the P^T and dS^T
 //     registers are directly the A operands of dV += P^T dO and
 //     dK += dS^T Q; dO^T and Q^T come from LDS through ds_read_b64_tr_b16.
-//   * Q and dO tiles go straight into LDS (global_load_lds_dwordx4),
+//     Q and dO tiles go straight into swizzled LDS (global_load_lds_dwordx4),
 //     double-buffered; L_new and Delta of the 64 rows through registers.
+//     Per-lane LDS offsets are computed once and the loop is unrolled by two
+//     so buffer offsets are immediates.
+#include <type_traits>
+
 #include "qmajor.cuh"
 
 namespace sa {
@@ -30,8 +43,117 @@ using namespace qm;
 
 constexpr int BM = 64;            // query rows per iteration
 constexpr int NWK = 2;            // wavefronts per workgroup
+constexpr int kChunk = 128;       // iterations per work item
+constexpr int kMaxQueues = 8;
 
-__global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt,
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Number of work queues: one per XCD when KV heads spread evenly over 8.
+inline int num_queues(const Prefill& p) { return (p.hkv % kMaxQueues == 0) ? kMaxQueues : 1; }
+
+// Key tile ti <-> (b, kt, g): queue-major so each queue's tiles are
+// contiguous, then sample, key tile, and the KV heads of the queue.
+struct TileId {
+  int b, kt, g;
+};
+__device__ __forceinline__ TileId tile_of(const Prefill& p, int nkt, int nq, int ti) {
+  const int hq_per = p.hkv / nq;                   // KV heads per queue
+  const int per_q = p.batch * nkt * hq_per;
+  const int q = ti / per_q;
+  int r = ti % per_q;
+  TileId t;
+  t.b = r / (nkt * hq_per);
+  r %= nkt * hq_per;
+  t.kt = r / hq_per;
+  t.g = (r % hq_per) * nq + q;
+  return t;
+}
+
+// Iterations of key tile (b, kt, g): the query tiles [qt_begin, qt_end) or
+// the reverse block list, times the G query heads of the group.
+struct TileWork {
+  int per_head, qt_begin;
+  const int32_t* list;
+};
+__device__ __forceinline__ TileWork tile_work(const Prefill& p, const BwdWork& w, int b, int kt, int g,
+                                              int L) {
+  TileWork tw;
+  tw.list = nullptr;
+  tw.qt_begin = kt;
+  const int k0 = kt * BN;
+  if (k0 >= L) {
+    tw.per_head = 0;
+    return tw;
+  }
+  const int nqt = (L + BM - 1) / BM;
+  if (p.blocks != nullptr) {
+    const int idx = (q_block_offset(p.cu, b) + kt) * p.hkv + g;
+    tw.list = w.csr_idx + w.csr_off[idx];
+    tw.per_head = w.csr_off[idx + 1] - w.csr_off[idx];
+  } else {
+    int qt_end = nqt;
+    if (p.window > 0 && k0 >= p.n_sink) {
+      // no first token here: only queries with q - key < window see the tile
+      const int last_q = min(L - 1, k0 + BN - 1 + p.window - 1);
+      qt_end = last_q / BM + 1;
+    }
+    tw.per_head = qt_end - kt;
+  }
+  return tw;
+}
+
+// Chunks per key tile (an empty tile still gets one, which writes zeros).
+__global__ __launch_bounds__(256) void plan_kernel(Prefill p, BwdWork w, int nkt, int nq) {
+  const int ntiles = p.batch * nkt * p.hkv;
+  const int ti = blockIdx.x * blockDim.x + threadIdx.x;
+  if (ti < kMaxQueues && blockIdx.x == 0) w.queues[ti] = 0;
+  if (ti >= ntiles) return;
+  const TileId t = tile_of(p, nkt, nq, ti);
+  const int L = p.cu[t.b + 1] - p.cu[t.b];
+  int chunks = 0;
+  if (t.kt * BN < L) {
+    const TileWork tw = tile_work(p, w, t.b, t.kt, t.g, L);
+    const int n = tw.per_head * (p.hq / p.hkv);
+    chunks = max(1, (n + kChunk - 1) / kChunk);
+  }
+  w.plan[ti + 1] = chunks;
+}
+
+// Zero (before) and convert (after) the float32 accumulators of split tiles.
+template <bool kConvert>
+__global__ __launch_bounds__(256) void split_tiles_kernel(Prefill p, BwdWork w, int nkt, int nq,
+                                                          uint16_t* __restrict__ dK,
+                                                          uint16_t* __restrict__ dV) {
+  const int ti = blockIdx.x;
+  if (w.plan[ti + 1] - w.plan[ti] <= 1) return;
+  const TileId t = tile_of(p, nkt, nq, ti);
+  const int t0 = p.cu[t.b];
+  const int L = p.cu[t.b + 1] - t0;
+  const int rows = min(BN, L - t.kt * BN);
+  for (int e = threadIdx.x; e < rows * D; e += blockDim.x) {
+    const size_t o = (static_cast<size_t>(t0 + t.kt * BN + e / D) * p.hkv + t.g) * D + e % D;
+    if (kConvert) {
+      dK[o] = f32_to_bf16(w.dk_acc[o]);
+      dV[o] = f32_to_bf16(w.dv_acc[o]);
+    } else {
+      w.dk_acc[o] = 0.f;
+      w.dv_acc[o] = 0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const lds_char* base, int byte_off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + byte_off));
+}
+__device__ __forceinline__ bf16x8 lds_tr_pair(const lds_char* base, int off_a, int off_b) {
+  const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (__attribute__((address_space(3))) i16x4*)(base + off_a)));
+  const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (__attribute__((address_space(3))) i16x4*)(base + off_b)));
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+__global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq,
                                                       const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ K,
                                                       const uint16_t* __restrict__ V,
@@ -42,19 +164,7 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt,
   __shared__ __attribute__((aligned(16))) uint16_t dobuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float lbuf[2][BM];
   __shared__ __attribute__((aligned(16))) float dbuf[2][BM];
-
-  // Flat block id -> (key tile, sample, KV head), key tiles ascending: the
-  // tiles with the most query rows (early causal tiles, first-token tiles)
-  // start first.
-  const int per_kt = p.batch * p.hkv;
-  const int kt = blockIdx.x / per_kt;
-  const int b = (blockIdx.x % per_kt) / p.hkv;
-  const int g = blockIdx.x % p.hkv;
-  (void)nkt;
-  const int t0 = p.cu[b];
-  const int L = p.cu[b + 1] - t0;
-  const int k0 = kt * BN;
-  if (k0 >= L) return;
+  __shared__ int item_sh;
 
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
@@ -62,168 +172,212 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt,
   const int l32 = lane & 31;
   const int gq = lane >> 5;
   const int G = p.hq / p.hkv;
-  const int kw0 = k0 + 32 * wv;         // this wavefront's first key
   const size_t kvs = static_cast<size_t>(p.hkv) * D;
   const size_t qst = static_cast<size_t>(p.hq) * D;
-
-  // ---- query tiles that can see this key tile ----
-  const int nqt = (L + BM - 1) / BM;
-  int qt_begin = kt, qt_end = nqt;                  // causal
-  const int32_t* list = nullptr;
-  int list_n = 0;
-  if (p.blocks != nullptr) {
-    const int idx = (q_block_offset(p.cu, b) + kt) * p.hkv + g;
-    list = w.csr_idx + w.csr_off[idx];
-    list_n = w.csr_off[idx + 1] - w.csr_off[idx];
-  } else if (p.window > 0 && k0 >= p.n_sink) {
-    // no first token here: only queries with q - key < window see the tile
-    const int last_q = min(L - 1, k0 + BN - 1 + p.window - 1);
-    qt_end = last_q / BM + 1;
-  }
-  const int per_head = p.blocks ? list_n : (qt_end - qt_begin);
-  const int n_iter = G * per_head;
-
-  // ---- K, V as B operands (lane: key kw0 + l32, dims gq*64 + ks*8) ----
-  bf16x8 kB[8], vB[8];
-  {
-    const int key = kw0 + l32;
-    const bool ok = key < L;
-    const uint16_t* ks_ = K + static_cast<size_t>(t0 + (ok ? key : 0)) * kvs + g * D + gq * 64;
-    const uint16_t* vs_ = V + static_cast<size_t>(t0 + (ok ? key : 0)) * kvs + g * D + gq * 64;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kB[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks_ + ks * 8))
-                  : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      vB[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vs_ + ks * 8))
-                  : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
-  }
-
-  f32x16 dKacc[4], dVacc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { dKacc[nt][i] = 0.f; dVacc[nt][i] = 0.f; }
-
   const float c_l2 = p.scale * kLog2e;
 
-  auto coord = [&](int it, int* h, int* qt) {
-    const int hh = it / per_head;
-    const int n = it % per_head;
-    *h = g * G + hh;
-    *qt = p.blocks ? list[n] : qt_begin + n;
-  };
-  // L_new (wavefront 0) or Delta (wavefront 1) of row `lane` of the tile:
-  // Hq floats apart in memory, so they go through a register into LDS.
-  auto load_ld = [&](int it) -> float {
-    int h, qt;
-    coord(it, &h, &qt);
-    const int q0 = qt * BM;
-    const int row = min(lane, min(BM, L - q0) - 1);
-    const size_t idx = static_cast<size_t>(t0 + q0 + row) * p.hq + h;
-    return wv == 0 ? w.lnew[idx] : w.delta[idx];
-  };
-  auto store_ld = [&](int buf, float x) {
-    if (wv == 0) lbuf[buf][lane] = x;
-    else dbuf[buf][lane] = x;
-  };
-  auto issue = [&](int it, int buf) {
-    int h, qt;
-    coord(it, &h, &qt);
-    const int q0 = qt * BM;
-    const int nvalid = min(BM, L - q0);
-    load_tile_lds(Q + static_cast<size_t>(t0 + q0) * qst + h * D, qst, nvalid, qbuf[buf], wv, NWK, lane);
-    load_tile_lds(dO + static_cast<size_t>(t0 + q0) * qst + h * D, qst, nvalid, dobuf[buf], wv, NWK, lane);
-  };
-
-  if (n_iter > 0) {
-    const float x = load_ld(0);
-    issue(0, 0);
-    store_ld(0, x);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    const bool has_next = it + 1 < n_iter;
-    float ld_next = 0.f;
-    if (has_next) {
-      ld_next = load_ld(it + 1);
-      issue(it + 1, buf ^ 1);
+  // Per-lane swizzled LDS byte offsets: row fragments (rows 32mt + l32,
+  // logical chunk gq*8 + ks) and transposed fragments (rows 16c + ra0 and
+  // +8, dims nt*32 + d4) of a staged 64 x 256-byte tile.
+  int roff[8], toa[4], tob[4];
+  {
+    const int sk = swz16(l32);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) roff[ks] = l32 * 256 + (((gq * 8 + ks) ^ sk) << 4);
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int ra0 = 4 * (grp >> 1) + (l16 >> 2);
+    const int d4 = 16 * (grp & 1) + 4 * (l16 & 3);
+    const int c4 = d4 >> 3, off = (d4 & 7) * 2;
+    const int sa_ = swz16(ra0), sb_ = swz16(ra0 + 8);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      toa[nt] = ra0 * 256 + (((nt * 4 + c4) ^ sa_) << 4) + off;
+      tob[nt] = (ra0 + 8) * 256 + (((nt * 4 + c4) ^ sb_) << 4) + off;
     }
-    int h, qt;
-    coord(it, &h, &qt);
-    const int q0 = qt * BM;
-    const int q1 = min(L, q0 + BM);
-    int cls = classify_tile(q0, q1, kw0, 32, p.n_sink, p.window);
-    if (cls == 1 && q1 - q0 < BM) cls = 2;          // rows past the sample must be masked
-    if (cls != 0) {
-      const uint16_t* qs = qbuf[buf];
-      const uint16_t* dos = dobuf[buf];
-      // S = Q K^T, dP = dO V^T : M = query rows (2 tiles), N = this wave's 32 keys
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { sacc[mt][i] = 0.f; pacc[mt][i] = 0.f; }
-        const int row = 32 * mt + l32;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sacc[mt] = mfma32(row_frag(qs, row, gq * 8 + ks), kB[ks], sacc[mt]);
-          pacc[mt] = mfma32(row_frag(dos, row, gq * 8 + ks), vB[ks], pacc[mt]);
-        }
-      }
-      // P = e^{x - L_new}; dS = P (dP - Delta).  Element i of lane (l32, gq)
-      // in M-tile mt: query row 32mt + 8(i/4) + 4gq + i%4, key kw0 + l32.
+  }
+
+  const int queue = blockIdx.x % nq;
+  const int tiles_per_q = p.batch * nkt * (p.hkv / nq);
+  const int item_lo = w.plan[queue * tiles_per_q];
+  const int item_hi = w.plan[(queue + 1) * tiles_per_q];
+
+  for (;;) {
+    if (tid == 0) item_sh = item_lo + atomicAdd(&w.queues[queue], 1);
+    __syncthreads();
+    const int item = item_sh;
+    __syncthreads();
+    if (item >= item_hi) break;
+
+    // item -> (tile, chunk): the tile whose plan range holds it
+    int lo = queue * tiles_per_q, hi = (queue + 1) * tiles_per_q - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (w.plan[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int ti = lo;
+    const int chunk = item - w.plan[ti];
+    const bool split = (w.plan[ti + 1] - w.plan[ti]) > 1;
+    const TileId t = tile_of(p, nkt, nq, ti);
+    const int b = t.b, kt = t.kt, g = t.g;
+    const int t0 = p.cu[b];
+    const int L = p.cu[b + 1] - t0;
+    const int k0 = kt * BN;
+    const int kw0 = k0 + 32 * wv;                 // this wavefront's first key
+    const TileWork tw = tile_work(p, w, b, kt, g, L);
+    const int n_all = G * tw.per_head;
+    const int it_begin = chunk * kChunk;
+    const int it_end = min(n_all, it_begin + kChunk);
+
+    // K, V as B operands (lane: key kw0 + l32, dims gq*64 + ks*8)
+    bf16x8 kB[8], vB[8];
+    {
       const int key = kw0 + l32;
+      const bool ok = key < L;
+      const uint16_t* ks_ = K + static_cast<size_t>(t0 + (ok ? key : 0)) * kvs + g * D + gq * 64;
+      const uint16_t* vs_ = V + static_cast<size_t>(t0 + (ok ? key : 0)) * kvs + g * D + gq * 64;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int ks = 0; ks < 8; ++ks) {
+        kB[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ks_ + ks * 8))
+                    : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        vB[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vs_ + ks * 8))
+                    : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
+    }
+    f32x16 dKacc[4], dVacc[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r0 = 32 * mt + 8 * u + 4 * gq;
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(&lbuf[buf][r0]);
-          const f32x4 dv = *reinterpret_cast<const f32x4*>(&dbuf[buf][r0]);
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * u + e;
-            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
-            if (cls == 2) {
-              const int qi = q0 + r0 + e;
-              if (!(qi < L && key_visible(qi, key, p.n_sink, p.window))) pe = 0.f;
+      for (int i = 0; i < 16; ++i) { dKacc[nt][i] = 0.f; dVacc[nt][i] = 0.f; }
+
+    auto coord = [&](int it, int* h, int* qt) {
+      const int hh = it / tw.per_head;
+      const int n = it % tw.per_head;
+      *h = g * G + hh;
+      *qt = tw.list ? tw.list[n] : tw.qt_begin + n;
+    };
+    // L_new (wavefront 0) or Delta (wavefront 1) of row `lane` of the tile:
+    // Hq floats apart in memory, so they go through a register into LDS.
+    auto load_ld = [&](int it) -> float {
+      int h, qt;
+      coord(it, &h, &qt);
+      const int q0 = qt * BM;
+      const int row = min(lane, min(BM, L - q0) - 1);
+      const size_t idx = static_cast<size_t>(t0 + q0 + row) * p.hq + h;
+      return wv == 0 ? w.lnew[idx] : w.delta[idx];
+    };
+    auto store_ld = [&](int buf, float x) {
+      if (wv == 0) lbuf[buf][lane] = x;
+      else dbuf[buf][lane] = x;
+    };
+    auto issue = [&](int it, int buf) {
+      int h, qt;
+      coord(it, &h, &qt);
+      const int q0 = qt * BM;
+      const int nvalid = min(BM, L - q0);
+      load_tile_lds(Q + static_cast<size_t>(t0 + q0) * qst + h * D, qst, nvalid, qbuf[buf], wv, NWK, lane);
+      load_tile_lds(dO + static_cast<size_t>(t0 + q0) * qst + h * D, qst, nvalid, dobuf[buf], wv, NWK, lane);
+    };
+
+    // One iteration on LDS buffer BUF: S, dP, P, dS, dV += P^T dO, dK += dS^T Q.
+    auto body = [&](auto BUF, int it) {
+      constexpr int buf = decltype(BUF)::value;
+      const bool has_next = it + 1 < it_end;
+      float ld_next = 0.f;
+      if (has_next) {
+        ld_next = load_ld(it + 1);
+        issue(it + 1, buf ^ 1);
+      }
+      int h, qt;
+      coord(it, &h, &qt);
+      const int q0 = qt * BM;
+      const int q1 = min(L, q0 + BM);
+      int cls = classify_tile(q0, q1, kw0, 32, p.n_sink, p.window);
+      if (cls == 1 && q1 - q0 < BM) cls = 2;        // rows past the sample must be masked
+      if (cls != 0) {
+        const lds_char* qs = (const lds_char*)(qbuf[buf]);
+        const lds_char* dos = (const lds_char*)(dobuf[buf]);
+        // S = Q K^T, dP = dO V^T : M = query rows (2 tiles), N = this wave's 32 keys
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) { sacc[mt][i] = 0.f; pacc[mt][i] = 0.f; }
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            sacc[mt] = mfma32(lds_frag(qs, roff[ks] + mt * 8192), kB[ks], sacc[mt]);
+            pacc[mt] = mfma32(lds_frag(dos, roff[ks] + mt * 8192), vB[ks], pacc[mt]);
+          }
+        }
+        // P = e^{x - L_new}; dS = P (dP - Delta).  Element i of lane (l32, gq)
+        // in M-tile mt: query row 32mt + 8(i/4) + 4gq + i%4, key kw0 + l32.
+        const int key = kw0 + l32;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r0 = 32 * mt + 8 * u + 4 * gq;
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lbuf[buf][r0]);
+            const f32x4 dv = *reinterpret_cast<const f32x4*>(&dbuf[buf][r0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * u + e;
+              float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
+              if (cls == 2) {
+                const int qi = q0 + r0 + e;
+                if (!(qi < L && key_visible(qi, key, p.n_sink, p.window))) pe = 0.f;
+              }
+              sacc[mt][i] = pe;
+              pacc[mt][i] = pe * (pacc[mt][i] - dv[e]);
             }
-            sacc[mt][i] = pe;
-            pacc[mt][i] = pe * (pacc[mt][i] - dv[e]);
+          }
+        }
+        // dV += P^T dO and dK += dS^T Q: N = dims (4 tiles), K = 64 query rows.
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 pa = pack_kstep(sacc[c >> 1], c & 1);
+          const bf16x8 da = pack_kstep(pacc[c >> 1], c & 1);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            dVacc[nt] = mfma32(pa, lds_tr_pair(dos, toa[nt] + c * 4096, tob[nt] + c * 4096), dVacc[nt]);
+            dKacc[nt] = mfma32(da, lds_tr_pair(qs, toa[nt] + c * 4096, tob[nt] + c * 4096), dKacc[nt]);
           }
         }
       }
-      // dV += P^T dO and dK += dS^T Q: N = dims (4 tiles), K = 64 query rows.
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 pa = pack_kstep(sacc[c >> 1], c & 1);
-        const bf16x8 da = pack_kstep(pacc[c >> 1], c & 1);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          dVacc[nt] = mfma32(pa, tr_frag(dos, 16 * c, nt * 32, lane), dVacc[nt]);
-          dKacc[nt] = mfma32(da, tr_frag(qs, 16 * c, nt * 32, lane), dKacc[nt]);
-        }
-      }
-    }
-    if (has_next) store_ld(buf ^ 1, ld_next);
-    __syncthreads();
-  }
+      if (has_next) store_ld(buf ^ 1, ld_next);
+      __syncthreads();
+    };
 
-  // ---- write dK (alpha-scaled) and dV: lane (dim nt*32 + l32, gq) holds
-  //      keys kw0 + 8(i/4) + 4gq + i%4 of C tile nt.
+    if (it_begin < it_end) {
+      const float x = load_ld(it_begin);
+      issue(it_begin, 0);
+      store_ld(0, x);
+    }
+    __syncthreads();
+    for (int it = it_begin; it < it_end; it += 2) {
+      body(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < it_end) body(std::integral_constant<int, 1>{}, it + 1);
+    }
+
+    // Results: lane (dim nt*32 + l32, gq) holds keys kw0 + 8(i/4) + 4gq + i%4
+    // of C tile nt.  dK is alpha-scaled.
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int dim = nt * 32 + l32;
+    for (int nt = 0; nt < 4; ++nt) {
+      const int dim = nt * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kw0 + 8 * (i >> 2) + 4 * gq + (i & 3);
-      if (key < L) {
-        const size_t o = static_cast<size_t>(t0 + key) * kvs + g * D + dim;
-        dK[o] = f32_to_bf16(p.scale * dKacc[nt][i]);
-        dV[o] = f32_to_bf16(dVacc[nt][i]);
+      for (int i = 0; i < 16; ++i) {
+        const int key = kw0 + 8 * (i >> 2) + 4 * gq + (i & 3);
+        if (key < L) {
+          const size_t o = static_cast<size_t>(t0 + key) * kvs + g * D + dim;
+          if (split) {
+            __hip_atomic_fetch_add(w.dk_acc + o, p.scale * dKacc[nt][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(w.dv_acc + o, dVacc[nt][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            dK[o] = f32_to_bf16(p.scale * dKacc[nt][i]);
+            dV[o] = f32_to_bf16(dVacc[nt][i]);
+          }
+        }
       }
     }
   }
@@ -236,21 +390,38 @@ bool bwd_mfma_supported(const Prefill& p) {
          (p.blocks == nullptr || p.max_seqlen <= qm::MAX_BITMAP_WORDS * 32 * qm::BN);
 }
 
+int bwd_num_tiles(const Prefill& p) {
+  const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
+  return p.batch * nkt * p.hkv;
+}
+
 hipError_t launch_bwd_dq(const Prefill& p, const void* q, const void* k, const void* v,
                          const void* dout, const BwdWork& w, void* dq, hipStream_t st);
+hipError_t launch_scan(int32_t* off, int n, hipStream_t st);
 
 hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
                            const void* dout, const BwdWork& w, void* dq, void* dk, void* dv,
                            hipStream_t st) {
   if (p.total == 0 || p.batch == 0) return hipSuccess;
   const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
-  const long long grid = static_cast<long long>(nkt) * p.batch * p.hkv;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd128::dkdv_kernel, dim3(static_cast<unsigned>(grid)), dim3(128), 0, st, p,
-                     nkt, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), w,
-                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv));
-  hipError_t e = hipGetLastError();
+  const int ntiles = p.batch * nkt * p.hkv;
+  if (ntiles <= 0) return hipSuccess;
+  const int nq = bwd128::num_queues(p);
+  uint16_t* dK = static_cast<uint16_t*>(dk);
+  uint16_t* dV = static_cast<uint16_t*>(dv);
+  hipLaunchKernelGGL(bwd128::plan_kernel, dim3((ntiles + 255) / 256), dim3(256), 0, st, p, w, nkt, nq);
+  hipError_t e = launch_scan(w.plan, ntiles, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd128::split_tiles_kernel<false>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,
+                     dK, dV);
+  // Persistent: two 2-wavefront workgroups per CU, a multiple of the queues.
+  const int grid = 512;
+  hipLaunchKernelGGL(bwd128::dkdv_kernel, dim3(grid), dim3(128), 0, st, p, nkt, nq,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), w, dK, dV);
+  hipLaunchKernelGGL(bwd128::split_tiles_kernel<true>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,
+                     dK, dV);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_bwd_dq(p, q, k, v, dout, w, dq, st);
 }

@@ -33,6 +33,8 @@ struct BwdWork {
   float* dv_acc;     // [T, Hkv, D]
   int32_t* csr_off;  // [nqb*Hkv + 1]  (block mode) per (KV block, KV head) list offsets
   int32_t* csr_idx;  // [nqb*Hkv*max_blocks] query blocks selecting each KV block
+  int32_t* plan;     // [batch*nkt*Hkv + 1] (MFMA path) chunks per key tile -> offsets
+  int32_t* queues;   // [8] work counters of the key-major pass
 };
 
 struct Decode {
@@ -60,6 +62,7 @@ hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const
                            const void* dout, const BwdWork& w, void* dq, void* dk, void* dv,
                            hipStream_t st);
 bool bwd_mfma_supported(const Prefill& p);
+int bwd_num_tiles(const Prefill& p);        // key tiles of the key-major pass
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st);
 hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq,
                              void* dk, void* dv, bool dq_from_acc, bool dkv_from_acc,

@@ -95,7 +95,7 @@ size_t elem_size(int dtype) { return dtype == SINK_ATTN_F32 ? 4 : 2; }
 
 // Backward workspace layout (each section 256-byte aligned).
 struct BwdLayout {
-  size_t delta, lnew, terms, dq_acc, dk_acc, dv_acc, csr_off, csr_idx, total;
+  size_t delta, lnew, terms, dq_acc, dk_acc, dv_acc, csr_off, csr_idx, plan, queues, total;
 };
 
 BwdLayout bwd_layout(const sa::Prefill& p) {
@@ -108,11 +108,13 @@ BwdLayout bwd_layout(const sa::Prefill& p) {
   l.lnew = off; off += round_up(rows * 4);
   l.terms = off; off += round_up(rows * 4);
   l.dq_acc = off;                                   // unused: dQ is stored directly
-  l.dk_acc = off; off += mfma ? 0 : round_up(kv * 4);
-  l.dv_acc = off; off += mfma ? 0 : round_up(kv * 4);
+  l.dk_acc = off; off += round_up(kv * 4);          // generic path; split key tiles
+  l.dv_acc = off; off += round_up(kv * 4);
   const size_t nl = p.blocks ? static_cast<size_t>(p.nqb) * p.hkv : 0;
   l.csr_off = off; off += (p.blocks && mfma) ? round_up((nl + 1) * 4) : 0;
   l.csr_idx = off; off += (p.blocks && mfma) ? round_up(nl * p.max_blocks * 4) : 0;
+  l.plan = off; off += mfma ? round_up((static_cast<size_t>(sa::bwd_num_tiles(p)) + 1) * 4) : 0;
+  l.queues = off; off += mfma ? round_up(8 * 4) : 0;
   l.total = off;
   return l;
 }
@@ -328,6 +330,8 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     w.dv_acc = reinterpret_cast<float*>(base + lay.dv_acc);
     w.csr_off = reinterpret_cast<int32_t*>(base + lay.csr_off);
     w.csr_idx = reinterpret_cast<int32_t*>(base + lay.csr_idx);
+    w.plan = reinterpret_cast<int32_t*>(base + lay.plan);
+    w.queues = reinterpret_cast<int32_t*>(base + lay.queues);
     const bool mfma = sa::bwd_mfma_supported(p);
     hipError_t e;
     if (mfma) {

@@ -62,6 +62,11 @@ FWD_CASES = {
     "no_sink": dict(lengths=(250, 99), hq=8, hkv=2, sink=False),
     "stress_sink": dict(lengths=(260,), hq=4, hkv=1, n_sink=4, window=64, sink_shift=4.0),
     "d64_generic": dict(lengths=(150, 40), hq=4, hkv=2, d=64),
+    # key tiles with more than 128 (head, query tile) iterations: the
+    # backward splits them over several work items
+    "dense_g8_long": dict(lengths=(1200, 70), hq=16, hkv=2),
+    "window_split": dict(lengths=(2200,), hq=8, hkv=1, n_sink=4, window=256),
+    "blocks_split": dict(lengths=(1500,), hq=16, hkv=2, block_lists=dict(n_random=4)),
 }
 
 
@@ -156,7 +161,7 @@ def test_q_zero_counts_closed_form():
 # ---------------------------------------------------------------------------
 
 BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "blocks_nodiag",
-             "d64_generic"]
+             "d64_generic", "dense_g8_long", "window_split", "blocks_split", "dense_g1", "window_g2"]
 
 
 @pytest.mark.parametrize("name", BWD_CASES)
