@@ -1,6 +1,6 @@
 """Benchmark of the sink-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--legs NAME]
 
 Prints ONE JSON line.  The headline (``value``) is the GQA prefill forward:
 4 packed samples x 4096 tokens, Hq=32, Hkv=8, D=128, bf16, causal, learnable
@@ -13,6 +13,7 @@ HIP events on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -24,6 +25,34 @@ import numpy as np
 METRIC = "sink-attn fwd/fwd+bwd TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+# HBM bytes one launch of the forward kernel moves on the GQA prefill
+# workload: rocprofv3 FETCH_SIZE and WRITE_SIZE passes (bench.py --legs
+# headline --calibrate-copy), each scaled by what the same counter reads for a
+# 1 GiB device-to-device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the
+# summary is profiles/fwd_kernel_gqa_prefill_4x4096.md.  The figures hold for
+# the kernel sources they were taken on: when those change, traffic is
+# reported as null until the counters are taken again.
+FWD_TRAFFIC = {
+    "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
+    "sha256": "a0e3f8dff5d343b3e986e22f4c8c6990624e2b1a4be80c3fa120aa05eeb68548",
+    "read_bytes": 219726796,
+    "write_bytes": 142607360,
+}
+
+
+def _fwd_traffic():
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "streamingllm_sink_attn_amd", "csrc")
+    h = hashlib.sha256()
+    try:
+        for f in FWD_TRAFFIC["sources"]:
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    except OSError:
+        return None
+    if h.hexdigest() != FWD_TRAFFIC["sha256"]:
+        return None
+    return FWD_TRAFFIC["read_bytes"] + FWD_TRAFFIC["write_bytes"]
 
 
 def _counts_window(lengths, n_sink, window):
@@ -264,7 +293,7 @@ def main():
     head = bench_gqa_prefill(torch, sa, W, args.steps, args.warmup)
     wl = head.pop("wl")
     roofline = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_BF16_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_BF16_TFLOPS, "traffic": _fwd_traffic()}
     line = {
         "metric": METRIC,
         "value": round(head["tflops"], 2),
