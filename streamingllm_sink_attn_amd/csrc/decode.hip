@@ -22,9 +22,10 @@
 //     16-byte chunks) and read back transposed with ds_read_b64_tr_b16, which
 //     gives each lane one dim at 4 slots: the A operand of O^T += V^T P^T.
 //   * The 4 wavefronts merge (m, l, acc) in LDS; the workgroup writes one
-//     partial per (b, head, split) to the workspace.
-// Merge kernel: M = max_k m_k, l = sum_k e^{m_k - M} l_k, L_orig = M + ln l,
-// O = s * sum_k e^{m_k - M} acc_k / l.
+//     partial per (b, head, split) to the workspace, or, with a single
+//     split, applies the sink epilogue itself and writes O, LSE and s.
+// Merge kernel (more than one split): M = max_k m_k, l = sum_k e^{m_k - M}
+// l_k, L_orig = M + ln l, O = s * sum_k e^{m_k - M} acc_k / l.
 #include "common.cuh"
 
 namespace sa {
@@ -68,7 +69,10 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
                                                        const uint16_t* __restrict__ Q,
                                                        const uint16_t* __restrict__ KC,
                                                        const uint16_t* __restrict__ VC,
-                                                       float* __restrict__ ws) {
+                                                       float* __restrict__ ws,
+                                                       uint16_t* __restrict__ O,
+                                                       float* __restrict__ lse,
+                                                       float* __restrict__ s_out) {
   // Per-wavefront double-buffered V chunks; after the loop the same memory
   // holds the wavefronts' partial results for the merge.
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][2][VBUF];
@@ -270,17 +274,44 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
         wgt[ww] = (mw == -kInf) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c);
         lt += wgt[ww] * mbuf[ww][hh][D + 1];
       }
-      float* dst = ws + ((static_cast<size_t>(b) * p.hq + h0 + hh) * p.splits + split) * (D + 2);
+      float a[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float a = 0.f;
+        a[e] = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) a += wgt[ww] * mbuf[ww][hh][d0 + e];
-        dst[d0 + e] = a;
+        for (int ww = 0; ww < NW; ++ww) a[e] += wgt[ww] * mbuf[ww][hh][d0 + e];
       }
-      if ((tid & 15) == 0) {
-        dst[D] = (M == -kInf) ? -kInf : M * p.scale;   // natural-log units
-        dst[D + 1] = lt;
+      const float Mn = (M == -kInf) ? -kInf : M * p.scale;   // natural-log units
+      if (p.splits == 1) {
+        // One split: this is the whole cache, so the sink epilogue of the
+        // merge runs here and no partial goes through the workspace.
+        const size_t r = static_cast<size_t>(b) * p.hq + h0 + hh;
+        float L_orig, s_val, mul;
+        if (lt > 0.f) {
+          L_orig = Mn + __logf(lt);
+          s_val = p.sink ? 1.f / (1.f + __expf(p.sink[h0 + hh] - L_orig)) : 1.f;
+          mul = s_val / lt;
+        } else {
+          L_orig = -kInf;
+          s_val = p.sink ? 0.f : 1.f;
+          mul = 0.f;
+        }
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(a[2 * e] * mul, a[2 * e + 1] * mul);
+        *reinterpret_cast<u32x4*>(O + r * D + d0) = pk;
+        if ((tid & 15) == 0) {
+          lse[r] = L_orig;
+          if (s_out) s_out[r] = s_val;
+        }
+      } else {
+        float* dst = ws + ((static_cast<size_t>(b) * p.hq + h0 + hh) * p.splits + split) * (D + 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[d0 + e] = a[e];
+        if ((tid & 15) == 0) {
+          dst[D] = Mn;
+          dst[D + 1] = lt;
+        }
       }
     }
   }
@@ -333,11 +364,14 @@ bool decode_mfma_supported(const Decode& p) {
 }
 
 int decode_auto_splits(const Decode& p) {
-  // Enough workgroups to keep every CU streaming (about 8 per CU), but no
-  // split shorter than 4 chunks per wavefront.
+  // One split (no merge pass) when the (sequence, KV head) units alone give
+  // every CU two workgroups; otherwise enough splits for about 8 per CU, but
+  // no split shorter than 4 chunks per wavefront.  Measured on 128 x 4096
+  // slots, 8 KV heads: 1 split 0.391 ms, 2: 0.410, 4: 0.420, 16: 0.436.
   const int G = p.hq / p.hkv;
   const long long units = static_cast<long long>(p.batch) * p.hkv * ((G + dec128::HN - 1) / dec128::HN);
   if (units <= 0) return 1;
+  if (units >= 512) return 1;
   long long want = (2048 + units - 1) / units;
   const long long max_by_len = p.slots / (dec128::CH * dec128::NW * 4);
   if (want > max_by_len) want = max_by_len;
@@ -354,9 +388,10 @@ hipError_t launch_decode(const Decode& p, const void* q, const void* kc, const v
   dim3 grid(p.splits, p.hkv * nhg, p.batch);
   hipLaunchKernelGGL(dec128::split_kernel, grid, dim3(256), 0, st, p, nhg,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), ws);
-  hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3(p.batch * p.hq), dim3(128), 0, st, p, ws, o,
-                     lse, s);
+                     static_cast<const uint16_t*>(vc), ws, static_cast<uint16_t*>(o), lse, s);
+  if (p.splits > 1)
+    hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3(p.batch * p.hq), dim3(128), 0, st, p, ws,
+                       o, lse, s);
   return hipGetLastError();
 }
 
