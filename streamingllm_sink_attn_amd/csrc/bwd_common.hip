@@ -5,7 +5,8 @@
 //     equation; s10 prefers e^{sink - lse_total} over 1 - s near s = 1);
 //   * the reverse block lists (per KV block: the query blocks selecting it),
 //     so that a KV-major backward visits each (KV block, query block) pair
-//     once and never adds the sink term per visit (s10);
+//     once and never adds the sink term per visit (s10), built through a
+//     selection bit matrix so the lists come out sorted;
 //   * finish: dsink as a fixed-order sum of the per-row terms (deterministic),
 //     and float32 accumulators converted to the output dtype.
 #include "common.cuh"
@@ -144,26 +145,47 @@ __device__ __forceinline__ void locate_block(const int32_t* cu, int batch, int k
   *b_out = batch - 1; *off_out = off;
 }
 
+// Bit matrix of the selections: word w of (global KV block kbg, KV head g)
+// holds bit qb % 32 for every sample-local query block qb in [32w, 32w + 32)
+// whose row selects the KV block (qb >= kb only; duplicates collapse).  One
+// thread per block-list entry.
+__global__ __launch_bounds__(256) void block_bits_kernel(Prefill p, BwdWork w, int words) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<size_t>(p.nqb) * p.hkv * p.max_blocks) return;
+  const int e = static_cast<int>(idx % p.max_blocks);
+  const int g = static_cast<int>((idx / p.max_blocks) % p.hkv);
+  const int qbg = static_cast<int>(idx / (static_cast<size_t>(p.max_blocks) * p.hkv));
+  int b, off;
+  locate_block(p.cu, p.batch, qbg, &b, &off);
+  const int qb = qbg - off;
+  const int nqb_b = (p.cu[b + 1] - p.cu[b] + kBlock - 1) / kBlock;
+  const int kb = p.blocks[(static_cast<size_t>(qbg) * p.hkv + g) * p.max_blocks + e];
+  if (kb < 0 || kb > qb || kb >= nqb_b || (qb >> 5) >= words) return;
+  atomicOr(w.csr_bits + (static_cast<size_t>(off + kb) * p.hkv + g) * words + (qb >> 5), 1u << (qb & 31));
+}
+
+// Per (KV block, KV head): the list length (kFill = false), or the list itself
+// in increasing query-block order (kFill = true, deterministic).
 template <bool kFill>
-__global__ __launch_bounds__(256) void block_csr_kernel(Prefill p, BwdWork w) {
+__global__ __launch_bounds__(256) void block_csr_kernel(Prefill p, BwdWork w, int words) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.nqb * p.hkv) return;
-  const int kbg = idx / p.hkv;
-  const int g = idx % p.hkv;
-  int b, off;
-  locate_block(p.cu, p.batch, kbg, &b, &off);
-  const int kb = kbg - off;
-  const int nqb_b = (p.cu[b + 1] - p.cu[b] + kBlock - 1) / kBlock;
+  const uint32_t* bits = w.csr_bits + static_cast<size_t>(idx) * words;
+  if (!kFill) {
+    int n = 0;
+    for (int i = 0; i < words; ++i) n += __builtin_popcount(bits[i]);
+    w.csr_off[idx + 1] = n;
+    return;
+  }
+  int32_t* dst = w.csr_idx + w.csr_off[idx];
   int n = 0;
-  int32_t* dst = kFill ? w.csr_idx + w.csr_off[idx] : nullptr;
-  for (int qb = kb; qb < nqb_b; ++qb) {
-    const int32_t* row = p.blocks + (static_cast<size_t>(off + qb) * p.hkv + g) * p.max_blocks;
-    if (row_selects(row, p.max_blocks, kb)) {
-      if (kFill) dst[n] = qb;
-      ++n;
+  for (int i = 0; i < words; ++i) {
+    uint32_t m = bits[i];
+    while (m != 0u) {
+      dst[n++] = 32 * i + __builtin_ctz(m);
+      m &= m - 1u;
     }
   }
-  if (!kFill) w.csr_off[idx + 1] = n;
 }
 
 // Exclusive scan of csr_off[1..n] in place (csr_off[0] = 0), one workgroup.
@@ -197,33 +219,69 @@ hipError_t launch_scan(int32_t* off, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
+int block_csr_words(const Prefill& p) {
+  const int max_nqb = (p.max_seqlen + kBlock - 1) / kBlock;
+  return (max_nqb + 31) / 32;
+}
+
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st) {
   const int n = p.nqb * p.hkv;
   if (n == 0) return hipSuccess;
+  const int words = block_csr_words(p);
+  const size_t nbits = static_cast<size_t>(n) * words;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(nbits, 1024)), dim3(256), 0, st,
+                     reinterpret_cast<float*>(w.csr_bits), nbits);
+  const size_t entries = static_cast<size_t>(n) * p.max_blocks;
+  hipLaunchKernelGGL(block_bits_kernel, dim3(static_cast<unsigned>((entries + 255) / 256)), dim3(256), 0,
+                     st, p, w, words);
   const int grid = (n + 255) / 256;
-  hipLaunchKernelGGL(block_csr_kernel<false>, dim3(grid), dim3(256), 0, st, p, w);
+  hipLaunchKernelGGL(block_csr_kernel<false>, dim3(grid), dim3(256), 0, st, p, w, words);
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, st, w.csr_off, n);
-  hipLaunchKernelGGL(block_csr_kernel<true>, dim3(grid), dim3(256), 0, st, p, w);
+  hipLaunchKernelGGL(block_csr_kernel<true>, dim3(grid), dim3(256), 0, st, p, w, words);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Finish: dsink[h] = sum_t terms[t, h] in a fixed order; accumulators -> dtype.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dsink_reduce_kernel(const float* __restrict__ terms, int T,
-                                                           int hq, float* __restrict__ dsink) {
+// Two passes, both in a fixed order: per slab of kDsinkRows rows, partial
+// sums of every head (reads are contiguous across the heads of a row), then
+// per head the sum of the slabs' partials.
+constexpr int kDsinkRows = 64;
+
+__global__ __launch_bounds__(256) void dsink_partial_kernel(const float* __restrict__ terms, int T,
+                                                            int hq, float* __restrict__ part) {
   __shared__ float red[256];
-  const int h = blockIdx.x;
-  float acc = 0.f;
-  for (int t = threadIdx.x; t < T; t += 256) acc += terms[static_cast<size_t>(t) * hq + h];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+  const int t0 = blockIdx.x * kDsinkRows;
+  const int t1 = min(T, t0 + kDsinkRows);
+  for (int hc = 0; hc < hq; hc += 256) {
+    const int ncol = min(256, hq - hc);
+    const int rpp = 256 / ncol;                       // rows per pass
+    const int r = threadIdx.x / ncol, h = threadIdx.x % ncol;
+    float acc = 0.f;
+    if (r < rpp)
+      for (int t = t0 + r; t < t1; t += rpp) acc += terms[static_cast<size_t>(t) * hq + hc + h];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < ncol) {
+      float sum = 0.f;
+      for (int k = 0; k < rpp; ++k) sum += red[k * ncol + threadIdx.x];
+      part[static_cast<size_t>(blockIdx.x) * hq + hc + threadIdx.x] = sum;
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) dsink[h] = red[0];
 }
+
+__global__ __launch_bounds__(256) void dsink_final_kernel(const float* __restrict__ part, int nslab,
+                                                          int hq, float* __restrict__ dsink) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= hq) return;
+  float acc = 0.f;
+  for (int k = 0; k < nslab; ++k) acc += part[static_cast<size_t>(k) * hq + h];
+  dsink[h] = acc;
+}
+
+int dsink_slabs(int total) { return (total + kDsinkRows - 1) / kDsinkRows; }
 
 template <typename T>
 __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, void* dst,
@@ -255,9 +313,14 @@ static void convert(const float* src, void* dst, size_t n, hipStream_t st) {
 
 hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq, void* dk,
                              void* dv, bool dq_from_acc, bool dkv_from_acc, hipStream_t st) {
-  if (dsink != nullptr)
-    hipLaunchKernelGGL(dsink_reduce_kernel, dim3(p.hq), dim3(256), 0, st, w.dsink_terms, p.total,
-                       p.hq, dsink);
+  if (dsink != nullptr) {
+    const int nslab = dsink_slabs(p.total);
+    if (nslab > 0)
+      hipLaunchKernelGGL(dsink_partial_kernel, dim3(nslab), dim3(256), 0, st, w.dsink_terms, p.total,
+                         p.hq, w.dsink_part);
+    hipLaunchKernelGGL(dsink_final_kernel, dim3((p.hq + 255) / 256), dim3(256), 0, st, w.dsink_part,
+                       nslab, p.hq, dsink);
+  }
   const size_t nq = static_cast<size_t>(p.total) * p.hq * p.d;
   const size_t nkv = static_cast<size_t>(p.total) * p.hkv * p.d;
   const bool f32 = p.dtype == SINK_ATTN_F32;

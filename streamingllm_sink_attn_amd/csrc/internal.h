@@ -28,11 +28,13 @@ struct BwdWork {
   float* delta;      // [T, Hq]  rowsum(dO * O)
   float* lnew;       // [T, Hq]  log(Z + e^a) (or L_orig; +inf for empty rows without a sink)
   float* dsink_terms;// [T, Hq]  -Delta * p_sink per row
+  float* dsink_part; // [ceil(T/64), Hq] per-slab partial sums of the terms
   float* dq_acc;     // [T, Hq, D]  (MFMA path) accumulated dQ
   float* dk_acc;     // [T, Hkv, D] (generic path, and the MFMA path's split sink tiles)
   float* dv_acc;     // [T, Hkv, D]
   int32_t* csr_off;  // [nqb*Hkv + 1]  (block mode) per (KV block, KV head) list offsets
   int32_t* csr_idx;  // [nqb*Hkv*max_blocks] query blocks selecting each KV block
+  uint32_t* csr_bits;// [nqb*Hkv*words] selection bit matrix the lists are built from
   int32_t* plan;     // [batch*nkt*Hkv + 1] (MFMA path) chunks per key tile -> offsets
   int32_t* queues;   // [8] work counters of the key-major pass
 };
@@ -64,6 +66,8 @@ hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const
 bool bwd_mfma_supported(const Prefill& p);
 int bwd_num_tiles(const Prefill& p);        // key tiles of the key-major pass
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st);
+int block_csr_words(const Prefill& p);      // 32-bit words per reverse-list bit row
+int dsink_slabs(int total);                 // row slabs of the dsink reduction
 hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq,
                              void* dk, void* dv, bool dq_from_acc, bool dkv_from_acc,
                              hipStream_t st);
