@@ -28,8 +28,10 @@
 //     v_mfma_f32_32x32x16_bf16 (lane column = key), so the P^T and dS^T
 //     registers are directly the A operands of dV += P^T dO and
 //     dK += dS^T Q; dO^T and Q^T come from LDS through ds_read_b64_tr_b16.
-//     Q and dO tiles go straight into swizzled LDS (global_load_lds_dwordx4),
-//     double-buffered; L_new and Delta of the 64 rows through registers.
+//     Q and dO tiles (and the L_new and Delta of their 64 rows) go straight
+//     into swizzled LDS, double-buffered: the next tile's loads are issued
+//     from asm blocks and waited for explicitly at the end of the iteration,
+//     so they overlap the whole current iteration.
 //     Per-lane LDS offsets are computed once and the loop is unrolled by two
 //     so buffer offsets are immediates.
 #include <type_traits>
@@ -164,16 +166,17 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
   __shared__ __attribute__((aligned(16))) uint16_t dobuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float lbuf[2][BM];
   __shared__ __attribute__((aligned(16))) float dbuf[2][BM];
+  __shared__ int qt_tab[kChunk];     // query tile of each iteration of the item
   __shared__ int item_sh;
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int gq = lane >> 5;
   const int G = p.hq / p.hkv;
   const size_t kvs = static_cast<size_t>(p.hkv) * D;
-  const size_t qst = static_cast<size_t>(p.hq) * D;
+  const int qst = p.hq * D;
   const float c_l2 = p.scale * kLog2e;
 
   // Per-lane swizzled LDS byte offsets: row fragments (rows 32mt + l32,
@@ -195,6 +198,23 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
       tob[nt] = (ra0 + 8) * 256 + (((nt * 4 + c4) ^ sb_) << 4) + off;
     }
   }
+
+  // This wavefront's share of a 64-row tile: 4-row blocks 8wv .. 8wv + 7.
+  uint32_t toff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 4 * (wv * 8 + j) + (lane >> 4);
+    const int lc = (lane & 15) ^ swz16(row);
+    toff[j] = static_cast<uint32_t>(row * qst + lc * 8) * 2u;
+  }
+  const uint32_t qbuf0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)(&qbuf[0][0])));
+  const uint32_t dobuf0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)(&dobuf[0][0])));
+  const uint32_t lbuf0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) float*)(&lbuf[0][0])));
+  const uint32_t dbuf0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) float*)(&dbuf[0][0])));
 
   const int queue = blockIdx.x % nq;
   const int tiles_per_q = p.batch * nkt * (p.hkv / nq);
@@ -243,6 +263,20 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
                     : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
       }
     }
+    // The operands must be in registers before any DMA of this item is in
+    // flight (the compiler counts only its own loads): consuming them here
+    // makes it wait for them before the loop rather than inside it.
+    asm volatile("" ::"v"(kB[0]), "v"(kB[1]), "v"(kB[2]), "v"(kB[3]), "v"(kB[4]), "v"(kB[5]),
+                 "v"(kB[6]), "v"(kB[7]));
+    asm volatile("" ::"v"(vB[0]), "v"(vB[1]), "v"(vB[2]), "v"(vB[3]), "v"(vB[4]), "v"(vB[5]),
+                 "v"(vB[6]), "v"(vB[7]));
+    // Query tiles of the item's iterations, read from the reverse list once
+    // (the loop then issues no vector memory operation besides the DMA).
+    for (int j = tid; j < it_end - it_begin; j += 64 * NWK) {
+      const int n = (it_begin + j) % tw.per_head;
+      qt_tab[j] = tw.list ? tw.list[n] : tw.qt_begin + n;
+    }
+    __syncthreads();
     f32x16 dKacc[4], dVacc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -250,43 +284,44 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
       for (int i = 0; i < 16; ++i) { dKacc[nt][i] = 0.f; dVacc[nt][i] = 0.f; }
 
     auto coord = [&](int it, int* h, int* qt) {
-      const int hh = it / tw.per_head;
-      const int n = it % tw.per_head;
-      *h = g * G + hh;
-      *qt = tw.list ? tw.list[n] : tw.qt_begin + n;
+      *h = g * G + it / tw.per_head;
+      *qt = qt_tab[it - it_begin];
     };
-    // L_new (wavefront 0) or Delta (wavefront 1) of row `lane` of the tile:
-    // Hq floats apart in memory, so they go through a register into LDS.
-    auto load_ld = [&](int it) -> float {
-      int h, qt;
-      coord(it, &h, &qt);
-      const int q0 = qt * BM;
-      const int row = min(lane, min(BM, L - q0) - 1);
-      const size_t idx = static_cast<size_t>(t0 + q0 + row) * p.hq + h;
-      return wv == 0 ? w.lnew[idx] : w.delta[idx];
-    };
-    auto store_ld = [&](int buf, float x) {
-      if (wv == 0) lbuf[buf][lane] = x;
-      else dbuf[buf][lane] = x;
-    };
+    // Stage the Q / dO tile and the L_new (wavefront 0) or Delta (wavefront
+    // 1) rows of iteration it in buffer buf: direct-to-LDS buffer loads from
+    // asm blocks (the compiler, which cannot see which LDS bytes they fill,
+    // would otherwise wait for them before the current tile's reads).  A
+    // ragged tile reads its last row in place of the missing ones.
     auto issue = [&](int it, int buf) {
       int h, qt;
       coord(it, &h, &qt);
       const int q0 = qt * BM;
-      const int nvalid = min(BM, L - q0);
-      load_tile_lds(Q + static_cast<size_t>(t0 + q0) * qst + h * D, qst, nvalid, qbuf[buf], wv, NWK, lane);
-      load_tile_lds(dO + static_cast<size_t>(t0 + q0) * qst + h * D, qst, nvalid, dobuf[buf], wv, NWK, lane);
+      const int rows = min(BM, L - q0);
+      const size_t r0 = static_cast<size_t>(t0 + q0);
+      const u32x4 rq = make_rsrc(Q + r0 * qst + h * D, static_cast<uint32_t>(rows * qst * 2));
+      const u32x4 rd = make_rsrc(dO + r0 * qst + h * D, static_cast<uint32_t>(rows * qst * 2));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t o = toff[j];
+        if (rows < BM) {
+          const int row = 4 * (wv * 8 + j) + (lane >> 4);
+          const int lc = (lane & 15) ^ swz16(row);
+          o = static_cast<uint32_t>(min(row, rows - 1) * qst + lc * 8) * 2u;
+        }
+        const uint32_t blk = static_cast<uint32_t>(buf * TILE + 4 * (wv * 8 + j) * D) * 2u;
+        dma16(rq, o, qbuf0 + blk);
+        dma16(rd, o, dobuf0 + blk);
+      }
+      const float* src = (wv == 0 ? w.lnew : w.delta) + r0 * p.hq + h;
+      const u32x4 rs = make_rsrc(src, static_cast<uint32_t>(rows * p.hq * 4));
+      dma4(rs, static_cast<uint32_t>(min(lane, rows - 1) * p.hq) * 4u,
+           (wv == 0 ? lbuf0 : dbuf0) + static_cast<uint32_t>(buf * BM * 4));
     };
 
     // One iteration on LDS buffer BUF: S, dP, P, dS, dV += P^T dO, dK += dS^T Q.
     auto body = [&](auto BUF, int it) {
       constexpr int buf = decltype(BUF)::value;
-      const bool has_next = it + 1 < it_end;
-      float ld_next = 0.f;
-      if (has_next) {
-        ld_next = load_ld(it + 1);
-        issue(it + 1, buf ^ 1);
-      }
+      if (it + 1 < it_end) issue(it + 1, buf ^ 1);
       int h, qt;
       coord(it, &h, &qt);
       const int q0 = qt * BM;
@@ -343,16 +378,13 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
           }
         }
       }
-      if (has_next) store_ld(buf ^ 1, ld_next);
-      __syncthreads();
+      // Next tile landed (each wavefront waits for its own loads) and no
+      // read of this buffer is in flight when it is refilled.
+      wait_bar<0>();
     };
 
-    if (it_begin < it_end) {
-      const float x = load_ld(it_begin);
-      issue(it_begin, 0);
-      store_ld(0, x);
-    }
-    __syncthreads();
+    if (it_begin < it_end) issue(it_begin, 0);
+    wait_bar<0>();
     for (int it = it_begin; it < it_end; it += 2) {
       body(std::integral_constant<int, 0>{}, it);
       if (it + 1 < it_end) body(std::integral_constant<int, 1>{}, it + 1);
@@ -382,6 +414,7 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
     }
   }
 }
+
 
 }  // namespace bwd128
 
@@ -415,8 +448,7 @@ hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const
   hipLaunchKernelGGL(bwd128::split_tiles_kernel<false>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,
                      dK, dV);
   // Persistent: two 2-wavefront workgroups per CU, a multiple of the queues.
-  const int grid = 512;
-  hipLaunchKernelGGL(bwd128::dkdv_kernel, dim3(grid), dim3(128), 0, st, p, nkt, nq,
+  hipLaunchKernelGGL(bwd128::dkdv_kernel, dim3(512), dim3(128), 0, st, p, nkt, nq,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), w, dK, dV);
   hipLaunchKernelGGL(bwd128::split_tiles_kernel<true>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,

@@ -168,6 +168,66 @@ __device__ __forceinline__ void load_tile_lds(const uint16_t* base, size_t row_s
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS buffer loads issued from asm blocks.  With the compiler's own
+// LDS-DMA intrinsics it cannot tell which LDS bytes a load fills, so it waits
+// for every such load before the wavefront's next LDS read; a tile prefetched
+// for the next iteration would then be waited for before the current one is
+// computed.  Issued from asm the loads stay in flight until the caller waits
+// for them (s_waitcnt vmcnt) and passes a barrier (wait_bar, which also waits
+// for the wavefront's own LDS reads so no read of a buffer is in flight when
+// it is refilled).  The compiler counts only its own vector memory
+// operations: loops that use these loads must issue no other vector memory
+// operation between issue and wait, and operands loaded before them are
+// consumed (or waited for) before the first one is issued.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu);   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+// One direct-to-LDS load: lane bytes (16 or 4) go to LDS m0 + lane * size.
+// An M0 write needs one wait state before an LDS DMA reads it.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);    // wave-uniform
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);    // wave-uniform
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+// Waits until at most N of this wavefront's vector memory operations are in
+// flight, then for its LDS reads, then passes the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_bar() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // 16-byte row fragment (8 consecutive dims of one row) of a staged tile.
 __device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int row, int lc) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + at16(row, lc)));
