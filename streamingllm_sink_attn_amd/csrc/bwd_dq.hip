@@ -28,7 +28,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
                                                     const uint16_t* __restrict__ dO, BwdWork w,
                                                     uint16_t* __restrict__ dQ) {
   __shared__ __attribute__((aligned(16))) uint16_t kv[2][2][TILE];   // [stage][K, V]
-  __shared__ uint32_t bitmap[MAX_BITMAP_WORDS];
+  __shared__ uint32_t bitmap[BITMAP_LDS_WORDS];
 
   const WgCoord wc = wg_coord(geo, p.batch, blockIdx.x);
   const int t0 = p.cu[wc.b];
@@ -72,6 +72,12 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
       dof[ks] = qf[ks];
     }
   }
+  // Loaded before any tile DMA is in flight (the compiler counts only its own
+  // loads): consuming them here makes it wait for them up front.
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
+               "v"(qf[6]), "v"(qf[7]));
+  asm volatile("" ::"v"(dof[0]), "v"(dof[1]), "v"(dof[2]), "v"(dof[3]), "v"(dof[4]), "v"(dof[5]),
+               "v"(dof[6]), "v"(dof[7]), "v"(Lq), "v"(Dq));
   const float lb = Lq * kLog2e;
 
   Sched sc = make_sched(p, L, qoff, g, p0, p1, bitmap);
@@ -83,25 +89,27 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[dt][i] = 0.f;
 
-  const size_t kvs = static_cast<size_t>(p.hkv) * D;
+  const int kvs = p.hkv * D;
   const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
   const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
+  DmaTiles<NWQ> ld;
+  ld.init(__builtin_amdgcn_readfirstlane(wv), lane, kvs);
+  const uint32_t kv0 = lds_address(&kv[0][0][0]);
   auto issue = [&](int kt, int st) {
     const int k0 = kt * BN;
-    const int nvalid = min(BN, L - k0);
-    load_tile_lds(Kg + static_cast<size_t>(k0) * kvs, kvs, nvalid, kv[st][0], wv, NWQ, lane);
-    load_tile_lds(Vg + static_cast<size_t>(k0) * kvs, kvs, nvalid, kv[st][1], wv, NWQ, lane);
+    ld.load(Kg + static_cast<size_t>(k0) * kvs, L - k0, kv0 + static_cast<uint32_t>((2 * st) * TILE * 2));
+    ld.load(Vg + static_cast<size_t>(k0) * kvs, L - k0, kv0 + static_cast<uint32_t>((2 * st + 1) * TILE * 2));
   };
 
   int kt = sc.next();
   if (kt >= 0) issue(kt, 0);
-  __syncthreads();
+  wait_bar<0>();
   int stage = 0;
   while (kt >= 0) {
     const int kt_next = sc.next();
     if (kt_next >= 0) issue(kt_next, stage ^ 1);
 
-    const int cls = wave_tile_class(p, qoff, g, wq0, wq1, kt);
+    const int cls = wave_tile_class(p, sc, p0, wq0, wq1, kt);
     if (cls != 0) {
       const uint16_t* Ks = kv[stage][0];
       const uint16_t* Vs = kv[stage][1];
@@ -139,7 +147,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
         for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma32(tr_frag(Ks, 16 * cc, dt * 32, lane), dsb, dqacc[dt]);
       }
     }
-    __syncthreads();
+    // The next tile landed and no read of this stage is in flight when it is
+    // refilled.
+    wait_bar<0>();
     stage ^= 1;
     kt = kt_next;
   }

@@ -8,7 +8,8 @@
 // Work decomposition (geometry and schedule in qmajor.cuh):
 //   * A workgroup is 8 wavefronts (2 per SIMD) of one KV head; each
 //     wavefront owns 32 query rows of one query head.  Keys come in 64-key
-//     tiles loaded straight into LDS (global_load_lds_dwordx4), and only the
+//     tiles loaded straight into LDS (buffer loads issued from asm blocks so
+//     they overlap a whole step; see qmajor.cuh), and only the
 //     tiles the mask can reach are visited: every causal tile, or the
 //     first-token tiles plus the window tiles, or the union of the selected
 //     blocks.  Each wavefront classifies a tile as empty (skipped), full, or
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
                                                           float* __restrict__ s_out) {
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][TILE];
-  __shared__ uint32_t bitmap[MAX_BITMAP_WORDS];
+  __shared__ uint32_t bitmap[BITMAP_LDS_WORDS];
 
   const WgCoord wc = wg_coord(geo, p.batch, blockIdx.x);
   const int t0 = p.cu[wc.b];
@@ -105,6 +106,10 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
+  // Loaded before any tile DMA is in flight (the compiler counts only its own
+  // loads): consuming the fragments here makes it wait for them up front.
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
+               "v"(qf[6]), "v"(qf[7]));
 
   // Per-lane swizzled LDS byte offsets (tile rows are 256 bytes).
   //   K fragment (mt, ks): row mt*32 + l32, logical chunk gq*8 + ks.
@@ -138,18 +143,21 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
   float mrun = -kInf, lsum = 0.f;
 
-  const size_t kvs = static_cast<size_t>(p.hkv) * D;
+  const int kvs = p.hkv * D;
   const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
   const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
+  DmaTiles<FNW> ld;
+  ld.init(__builtin_amdgcn_readfirstlane(w), lane, kvs);
+  const uint32_t kbuf0 = lds_address(&kbuf[0][0]), vbuf0 = lds_address(&vbuf[0][0]);
   auto issue_k = [&](int kt, int st) {
     const int k0 = kt * BN;
-    load_tile_lds(Kg + static_cast<size_t>(k0) * kvs, kvs, min(BN, L - k0), kbuf[st], w, FNW, lane);
+    ld.load(Kg + static_cast<size_t>(k0) * kvs, L - k0, kbuf0 + static_cast<uint32_t>(st * TILE * 2));
   };
   auto issue_v = [&](int kt, int st) {
     const int k0 = kt * BN;
-    load_tile_lds(Vg + static_cast<size_t>(k0) * kvs, kvs, min(BN, L - k0), vbuf[st], w, FNW, lane);
+    ld.load(Vg + static_cast<size_t>(k0) * kvs, L - k0, vbuf0 + static_cast<uint32_t>(st * TILE * 2));
   };
-  auto tile_class = [&](int kt) { return kt >= 0 ? wave_tile_class(p, qoff, g, wq0, wq1, kt) : 0; };
+  auto tile_class = [&](int kt) { return kt >= 0 ? wave_tile_class(p, sc, p0, wq0, wq1, kt) : 0; };
 
   // S^T of a tile from K buffer ST.
   auto scores = [&](auto ST, f32x16 (&s)[2]) {
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     issue_k(t_cur, 0);
     issue_v(t_cur, 0);
     if (t_nx >= 0) issue_k(t_nx, 1);
-    __syncthreads();
+    wait_bar<0>();
     bf16x8 pf[4];                                    // P of tile "cur" (bf16)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) pf[cc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -263,7 +271,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       finish_scores(t_cur, s0, pf);
       probs(s0, pf);
     }
-    __syncthreads();
+    wait_bar<0>();
 
     // One pipeline step: P of tile "cur" is in pf and its V in V buffer ST;
     // K of tile "nx" is in K buffer ST^1.  K of the tile after next goes to K
@@ -286,7 +294,9 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       } else {
         pv(std::integral_constant<int, st>{}, pf);
       }
-      __syncthreads();
+      // This step's loads landed and no read of the buffers they refill next
+      // step is in flight.
+      wait_bar<0>();
       t_cur = t_nx;
       t_nx = t_nx2;
     };
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
 // marking (query, key) pairs the forward visits and keeps.  One workgroup of
 // 256 threads per forward workgroup; out[b][g][i][j] for sample-local i, j.
 __global__ __launch_bounds__(256) void visit_map_kernel(Prefill p, Geo geo, uint8_t* out) {
-  __shared__ uint32_t bitmap[MAX_BITMAP_WORDS];
+  __shared__ uint32_t bitmap[BITMAP_LDS_WORDS];
   const WgCoord wc = wg_coord(geo, p.batch, blockIdx.x);
   if (wc.hg != 0) return;                        // the mask does not depend on the head group
   const int t0 = p.cu[wc.b];
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(256) void visit_map_kernel(Prefill p, Geo geo, uint
     for (int wv = 0; wv < geo.wph; ++wv) {
       const int wq0 = p0 + wv * FQW;
       const int wq1 = min(L, wq0 + FQW);
-      const int cls = wave_tile_class(p, qoff, wc.g, wq0, wq1, kt);
+      const int cls = wave_tile_class(p, sc, p0, wq0, wq1, kt);
       if (cls == 0) continue;
       for (int e = threadIdx.x; e < FQW * BN; e += blockDim.x) {
         const int qi = wq0 + e / BN;

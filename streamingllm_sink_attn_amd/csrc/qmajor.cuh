@@ -68,20 +68,29 @@ __device__ __forceinline__ WgCoord wg_coord(const Geo& geo, int batch, int bid) 
   return c;
 }
 
+// Block lists: one bitmap per query block of the workgroup (at most
+// MAX_QB_PER_WG; a workgroup's rows start on a block boundary), bit kb of row
+// j set when query block qb0 + j selects KV block kb (kb <= qb only).  Built
+// in LDS once, so classifying a tile inside the loop reads no global memory.
+constexpr int MAX_QB_PER_WG = 4;
+constexpr int BITMAP_LDS_WORDS = MAX_QB_PER_WG * MAX_BITMAP_WORDS;
+
 // The workgroup's key-tile schedule: ranges without block lists, else the
-// union bitmap of the selected blocks (built in LDS).
+// union of the query blocks' bitmaps.
 struct Sched {
   bool blk;
   TileRanges tr;
   int n;
-  int word, nwords;
+  int word, nwords, nrows;
   uint32_t bits;
   const uint32_t* bm;
   __device__ __forceinline__ int next() {
     if (!blk) return n < tr.count() ? tr.at(n++) : -1;
     while (bits == 0) {
       if (++word >= nwords) return -1;
-      bits = bm[word];
+      uint32_t u = 0u;
+      for (int j = 0; j < nrows; ++j) u |= bm[j * MAX_BITMAP_WORDS + word];
+      bits = u;
     }
     const int kb = word * 32 + __builtin_ctz(bits);
     bits &= bits - 1;
@@ -89,50 +98,58 @@ struct Sched {
   }
 };
 
-// Bitmap of the KV blocks selected by any query block in [p0, p1) (causal
-// blocks only).  Every thread of the workgroup must call it.
-__device__ __forceinline__ void build_block_bitmap(const Prefill& p, int L, int qoff, int g, int p0,
-                                                   int p1, uint32_t* bm, int* nwords_out) {
+// Bitmaps of the query blocks in [p0, p1) (p0 a multiple of BN).  Every
+// thread of the workgroup must call it.
+__device__ __forceinline__ void build_block_bitmaps(const Prefill& p, int L, int qoff, int g, int p0,
+                                                    int p1, uint32_t* bm, int* nwords_out,
+                                                    int* nrows_out) {
   const int nkb = (L + BN - 1) / BN;
   const int nwords = min((nkb + 31) / 32, MAX_BITMAP_WORDS);
-  for (int i = threadIdx.x; i < nwords; i += blockDim.x) bm[i] = 0u;
-  __syncthreads();
   const int qb0 = p0 / BN, qb1 = (p1 - 1) / BN;
-  const int total = (qb1 - qb0 + 1) * p.max_blocks;
+  const int nrows = min(qb1 - qb0 + 1, MAX_QB_PER_WG);
+  for (int i = threadIdx.x; i < nrows * nwords; i += blockDim.x)
+    bm[(i / nwords) * MAX_BITMAP_WORDS + i % nwords] = 0u;
+  __syncthreads();
+  const int total = nrows * p.max_blocks;
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int qb = qb0 + idx / p.max_blocks;
+    const int j = idx / p.max_blocks;
     const int e = idx % p.max_blocks;
+    const int qb = qb0 + j;
     const int kb = p.blocks[(static_cast<size_t>(qoff + qb) * p.hkv + g) * p.max_blocks + e];
-    if (kb >= 0 && kb <= qb && (kb >> 5) < nwords) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+    if (kb >= 0 && kb <= qb && (kb >> 5) < nwords)
+      atomicOr(&bm[j * MAX_BITMAP_WORDS + (kb >> 5)], 1u << (kb & 31));
   }
   __syncthreads();
   *nwords_out = nwords;
+  *nrows_out = nrows;
 }
 
+// bm holds BITMAP_LDS_WORDS words of LDS.
 __device__ __forceinline__ Sched make_sched(const Prefill& p, int L, int qoff, int g, int p0, int p1,
-                                            uint32_t* bitmap) {
+                                            uint32_t* bm) {
   Sched sc;
   sc.blk = p.blocks != nullptr;
   sc.n = 0;
   sc.word = -1;
   sc.bits = 0u;
-  sc.bm = bitmap;
+  sc.bm = bm;
   sc.nwords = 0;
-  if (sc.blk) build_block_bitmap(p, L, qoff, g, p0, p1, bitmap, &sc.nwords);
+  sc.nrows = 0;
+  if (sc.blk) build_block_bitmaps(p, L, qoff, g, p0, p1, bm, &sc.nwords, &sc.nrows);
   else sc.tr = window_tiles(p0, p1, p.n_sink, p.window, BN);
   return sc;
 }
 
-// Class of key tile kt for a wavefront's rows [wq0, wq1): 0 empty, 1 full,
-// 2 mixed.  With block lists the wavefront's own query block must select it.
-__device__ __forceinline__ int wave_tile_class(const Prefill& p, int qoff, int g, int wq0, int wq1,
-                                               int kt) {
+// Class of key tile kt for a wavefront's rows [wq0, wq1) (inside one query
+// block; p0 the workgroup's first row): 0 empty, 1 full, 2 mixed.  With block
+// lists the wavefront's own query block must select the tile.
+__device__ __forceinline__ int wave_tile_class(const Prefill& p, const Sched& sc, int p0, int wq0,
+                                               int wq1, int kt) {
   if (wq0 >= wq1) return 0;
   int cls = classify_tile(wq0, wq1, kt * BN, BN, p.n_sink, p.window);
-  if (cls != 0 && p.blocks != nullptr) {
-    const int32_t* row =
-        p.blocks + (static_cast<size_t>(qoff + wq0 / BN) * p.hkv + g) * p.max_blocks;
-    if (!row_selects(row, p.max_blocks, kt)) cls = 0;
+  if (cls != 0 && sc.blk) {
+    const int j = wq0 / BN - p0 / BN;
+    if (((sc.bm[j * MAX_BITMAP_WORDS + (kt >> 5)] >> (kt & 31)) & 1u) == 0u) cls = 0;
   }
   return cls;
 }
@@ -227,6 +244,48 @@ __device__ __forceinline__ void wait_bar() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(p)));
+}
+
+// 64-row tiles into swizzled LDS with dma16: wavefront wv of NWV owns the
+// 4-row blocks PER*wv .. PER*wv + PER - 1; per-lane offsets inside a full tile
+// are computed once, a ragged tile reads its last row in place of the
+// missing ones (finite data that the mask discards).
+template <int NWV>
+struct DmaTiles {
+  static constexpr int PER = 16 / NWV;
+  uint32_t off[PER];
+  int wv, lane, stride;
+  __device__ __forceinline__ void init(int wv_, int lane_, int row_stride) {
+    wv = wv_;
+    lane = lane_;
+    stride = row_stride;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int row = 4 * (wv * PER + j) + (lane >> 4);
+      const int lc = (lane & 15) ^ swz16(row);
+      off[j] = static_cast<uint32_t>(row * row_stride + lc * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void load(const uint16_t* base, int nvalid, uint32_t lds_tile) const {
+    const int rows = nvalid < BN ? nvalid : BN;
+    const u32x4 rsrc = make_rsrc(base, static_cast<uint32_t>(rows * stride * 2));
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      uint32_t o = off[j];
+      if (rows < BN) {
+        const int row = 4 * (wv * PER + j) + (lane >> 4);
+        const int lc = (lane & 15) ^ swz16(row);
+        o = static_cast<uint32_t>(min(row, rows - 1) * stride + lc * 8) * 2u;
+      }
+      dma16(rsrc, o, lds_tile + static_cast<uint32_t>(4 * (wv * PER + j) * D) * 2u);
+    }
+  }
+};
 
 // 16-byte row fragment (8 consecutive dims of one row) of a staged tile.
 __device__ __forceinline__ bf16x8 row_frag(const uint16_t* tile, int row, int lc) {
