@@ -127,16 +127,26 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
         }
       }
       // dS^T = P^T (dP^T - Delta); element i of lane (l32, gq) in M-tile mt is
-      // key k0 + 32mt + 8(i/4) + 4gq + i%4, query qi.
+      // key k0 + 32mt + 8(i/4) + 4gq + i%4, query qi.  A mixed tile first sets
+      // the scores of invisible pairs to -inf, so the exponentials run without
+      // a branch.
+      if (cls == 2) {
+        const int d = qi - k0;
+        const int lo = p.window > 0 ? d - p.window : -(1 << 30);
+        const int sk = p.window > 0 ? p.n_sink - k0 : -(1 << 30);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rel = mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
+            if (!(rel <= d && (rel > lo || rel < sk))) sacc[mt][i] = -kInf;
+          }
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c, -lb));
-          if (cls == 2) {
-            const int key = k0 + mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
-            if (!key_visible(qi, key, p.n_sink, p.window)) pe = 0.f;
-          }
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c, -lb));
           pacc[mt][i] = pe * (pacc[mt][i] - Dq);
         }
       // dQ^T += K^T dS^T : M = dims (4 tiles), N = 32 queries, K = 64 keys.

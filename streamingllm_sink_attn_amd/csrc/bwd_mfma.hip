@@ -343,9 +343,21 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
             pacc[mt] = mfma32(lds_frag(dos, roff[ks] + mt * 8192), vB[ks], pacc[mt]);
           }
         }
-        // P = e^{x - L_new}; dS = P (dP - Delta).  Element i of lane (l32, gq)
-        // in M-tile mt: query row 32mt + 8(i/4) + 4gq + i%4, key kw0 + l32.
-        const int key = kw0 + l32;
+        // Element i of lane (l32, gq) in M-tile mt: query row
+        // 32mt + 8(i/4) + 4gq + i%4, key kw0 + l32.  A mixed tile first sets
+        // the scores of invisible pairs to -inf (P = 0, so dS = 0), so the
+        // exponentials below run without a branch.
+        if (cls == 2) {
+          const int key = kw0 + l32;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int qi = q0 + 32 * mt + 8 * (i >> 2) + 4 * gq + (i & 3);
+              if (!(qi < L && key_visible(qi, key, p.n_sink, p.window))) sacc[mt][i] = -kInf;
+            }
+        }
+        // P = e^{x - L_new}; dS = P (dP - Delta).
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -356,11 +368,7 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * u + e;
-              float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
-              if (cls == 2) {
-                const int qi = q0 + r0 + e;
-                if (!(qi < L && key_visible(qi, key, p.n_sink, p.window))) pe = 0.f;
-              }
+              const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
               sacc[mt][i] = pe;
               pacc[mt][i] = pe * (pacc[mt][i] - dv[e]);
             }
