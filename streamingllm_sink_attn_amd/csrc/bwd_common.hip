@@ -272,13 +272,21 @@ __global__ __launch_bounds__(256) void dsink_partial_kernel(const float* __restr
   }
 }
 
+// One workgroup per head: thread t sums slabs t, t + 256, ... in order, then
+// a fixed tree over the 256 partial sums.
 __global__ __launch_bounds__(256) void dsink_final_kernel(const float* __restrict__ part, int nslab,
                                                           int hq, float* __restrict__ dsink) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= hq) return;
+  __shared__ float red[256];
+  const int h = blockIdx.x;
   float acc = 0.f;
-  for (int k = 0; k < nslab; ++k) acc += part[static_cast<size_t>(k) * hq + h];
-  dsink[h] = acc;
+  for (int k = threadIdx.x; k < nslab; k += 256) acc += part[static_cast<size_t>(k) * hq + h];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsink[h] = red[0];
 }
 
 int dsink_slabs(int total) { return (total + kDsinkRows - 1) / kDsinkRows; }
@@ -318,8 +326,8 @@ hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, v
     if (nslab > 0)
       hipLaunchKernelGGL(dsink_partial_kernel, dim3(nslab), dim3(256), 0, st, w.dsink_terms, p.total,
                          p.hq, w.dsink_part);
-    hipLaunchKernelGGL(dsink_final_kernel, dim3((p.hq + 255) / 256), dim3(256), 0, st, w.dsink_part,
-                       nslab, p.hq, dsink);
+    hipLaunchKernelGGL(dsink_final_kernel, dim3(p.hq), dim3(256), 0, st, w.dsink_part, nslab, p.hq,
+                       dsink);
   }
   const size_t nq = static_cast<size_t>(p.total) * p.hq * p.d;
   const size_t nkv = static_cast<size_t>(p.total) * p.hkv * p.d;

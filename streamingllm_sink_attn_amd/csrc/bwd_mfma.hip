@@ -321,28 +321,46 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
     // One iteration on LDS buffer BUF: S, dP, P, dS, dV += P^T dO, dK += dS^T Q.
     auto body = [&](auto BUF, int it) {
       constexpr int buf = decltype(BUF)::value;
-      if (it + 1 < it_end) issue(it + 1, buf ^ 1);
       int h, qt;
       coord(it, &h, &qt);
       const int q0 = qt * BM;
       const int q1 = min(L, q0 + BM);
       int cls = classify_tile(q0, q1, kw0, 32, p.n_sink, p.window);
       if (cls == 1 && q1 - q0 < BM) cls = 2;        // rows past the sample must be masked
+      f32x16 sacc[2], pacc[2];
       if (cls != 0) {
         const lds_char* qs = (const lds_char*)(qbuf[buf]);
         const lds_char* dos = (const lds_char*)(dobuf[buf]);
         // S = Q K^T, dP = dO V^T : M = query rows (2 tiles), N = this wave's 32 keys
-        f32x16 sacc[2], pacc[2];
+        // Fragments are read one step ahead of their MFMAs (order fixed by
+        // the scheduling barriers), so LDS latency overlaps the matrix core.
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) { sacc[mt][i] = 0.f; pacc[mt][i] = 0.f; }
+        {
+          bf16x8 fq[2], fd[2];
+          fq[0] = lds_frag(qs, roff[0]);
+          fd[0] = lds_frag(dos, roff[0]);
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            sacc[mt] = mfma32(lds_frag(qs, roff[ks] + mt * 8192), kB[ks], sacc[mt]);
-            pacc[mt] = mfma32(lds_frag(dos, roff[ks] + mt * 8192), vB[ks], pacc[mt]);
+          for (int x = 0; x < 16; ++x) {
+            const int mt = x >> 3, ks = x & 7;
+            if (x + 1 < 16) {
+              const int mt1 = (x + 1) >> 3, ks1 = (x + 1) & 7;
+              fq[(x + 1) & 1] = lds_frag(qs, roff[ks1] + mt1 * 8192);
+              fd[(x + 1) & 1] = lds_frag(dos, roff[ks1] + mt1 * 8192);
+            }
+            sacc[mt] = mfma32(fq[x & 1], kB[ks], sacc[mt]);
+            pacc[mt] = mfma32(fd[x & 1], vB[ks], pacc[mt]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
+      }
+      // The next tile's loads are issued behind this tile's first MFMAs.
+      if (it + 1 < it_end) issue(it + 1, buf ^ 1);
+      if (cls != 0) {
+        const lds_char* qs = (const lds_char*)(qbuf[buf]);
+        const lds_char* dos = (const lds_char*)(dobuf[buf]);
         // Element i of lane (l32, gq) in M-tile mt: query row
         // 32mt + 8(i/4) + 4gq + i%4, key kw0 + l32.  A mixed tile first sets
         // the scores of invisible pairs to -inf (P = 0, so dS = 0), so the
@@ -375,14 +393,27 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
           }
         }
         // dV += P^T dO and dK += dS^T Q: N = dims (4 tiles), K = 64 query rows.
+        bf16x8 pa[4], da[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bf16x8 pa = pack_kstep(sacc[c >> 1], c & 1);
-          const bf16x8 da = pack_kstep(pacc[c >> 1], c & 1);
+          pa[c] = pack_kstep(sacc[c >> 1], c & 1);
+          da[c] = pack_kstep(pacc[c >> 1], c & 1);
+        }
+        {
+          bf16x8 fv[2], fk[2];
+          fv[0] = lds_tr_pair(dos, toa[0], tob[0]);
+          fk[0] = lds_tr_pair(qs, toa[0], tob[0]);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            dVacc[nt] = mfma32(pa, lds_tr_pair(dos, toa[nt] + c * 4096, tob[nt] + c * 4096), dVacc[nt]);
-            dKacc[nt] = mfma32(da, lds_tr_pair(qs, toa[nt] + c * 4096, tob[nt] + c * 4096), dKacc[nt]);
+          for (int x = 0; x < 16; ++x) {
+            const int c = x >> 2, nt = x & 3;
+            if (x + 1 < 16) {
+              const int c1 = (x + 1) >> 2, nt1 = (x + 1) & 3;
+              fv[(x + 1) & 1] = lds_tr_pair(dos, toa[nt1] + c1 * 4096, tob[nt1] + c1 * 4096);
+              fk[(x + 1) & 1] = lds_tr_pair(qs, toa[nt1] + c1 * 4096, tob[nt1] + c1 * 4096);
+            }
+            dVacc[nt] = mfma32(pa[c], fv[x & 1], dVacc[nt]);
+            dKacc[nt] = mfma32(da[c], fk[x & 1], dKacc[nt]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
