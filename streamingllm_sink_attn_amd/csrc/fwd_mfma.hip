@@ -159,15 +159,24 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   };
   auto tile_class = [&](int kt) { return kt >= 0 ? wave_tile_class(p, sc, p0, wq0, wq1, kt) : 0; };
 
-  // S^T of a tile from K buffer ST.
+  // S^T of a tile from K buffer ST.  The two 32-key halves alternate (two
+  // independent accumulation chains) and every K fragment is read two MFMAs
+  // ahead, in an order the scheduling barriers keep.
   auto scores = [&](auto ST, f32x16 (&s)[2]) {
     const lds_char* kb = (const lds_char*)(kbuf[decltype(ST)::value]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[mt][i] = 0.f;
+    bf16x8 f[3];
+    f[0] = lds_frag(kb, koff[0]);
+    f[1] = lds_frag(kb, koff[0] + 8192);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[mt] = mfma32(lds_frag(kb, koff[ks] + mt * 8192), qf[ks], s[mt]);
+    for (int x = 0; x < 16; ++x) {
+      if (x + 2 < 16) f[(x + 2) % 3] = lds_frag(kb, koff[(x + 2) >> 1] + ((x + 2) & 1) * 8192);
+      __builtin_amdgcn_sched_barrier(0);
+      s[x & 1] = mfma32(f[x % 3], qf[x >> 1], s[x & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Element mask of a mixed tile: element i of M-tile mt is key
