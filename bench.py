@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
-    "sha256": "a0e3f8dff5d343b3e986e22f4c8c6990624e2b1a4be80c3fa120aa05eeb68548",
-    "read_bytes": 219726796,
-    "write_bytes": 142607360,
+    "sha256": "6d5042dd7116b00d1bf2b45f59e98febe59aeec5e700538ca8176d55a8bfc22e",
+    "read_bytes": 224091280,
+    "write_bytes": 142697003,
 }
 
 
