@@ -300,17 +300,23 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
       const size_t r0 = static_cast<size_t>(t0 + q0);
       const u32x4 rq = make_rsrc(Q + r0 * qst + h * D, static_cast<uint32_t>(rows * qst * 2));
       const u32x4 rd = make_rsrc(dO + r0 * qst + h * D, static_cast<uint32_t>(rows * qst * 2));
+      if (rows == BM) {                             // uniform: a full tile
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t o = toff[j];
-        if (rows < BM) {
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t blk = static_cast<uint32_t>(buf * TILE + 4 * (wv * 8 + j) * D) * 2u;
+          dma16(rq, toff[j], qbuf0 + blk);
+          dma16(rd, toff[j], dobuf0 + blk);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
           const int row = 4 * (wv * 8 + j) + (lane >> 4);
           const int lc = (lane & 15) ^ swz16(row);
-          o = static_cast<uint32_t>(min(row, rows - 1) * qst + lc * 8) * 2u;
+          const uint32_t o = static_cast<uint32_t>(min(row, rows - 1) * qst + lc * 8) * 2u;
+          const uint32_t blk = static_cast<uint32_t>(buf * TILE + 4 * (wv * 8 + j) * D) * 2u;
+          dma16(rq, o, qbuf0 + blk);
+          dma16(rd, o, dobuf0 + blk);
         }
-        const uint32_t blk = static_cast<uint32_t>(buf * TILE + 4 * (wv * 8 + j) * D) * 2u;
-        dma16(rq, o, qbuf0 + blk);
-        dma16(rd, o, dobuf0 + blk);
       }
       const float* src = (wv == 0 ? w.lnew : w.delta) + r0 * p.hq + h;
       const u32x4 rs = make_rsrc(src, static_cast<uint32_t>(rows * p.hq * 4));
@@ -361,37 +367,43 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
       if (cls != 0) {
         const lds_char* qs = (const lds_char*)(qbuf[buf]);
         const lds_char* dos = (const lds_char*)(dobuf[buf]);
-        // Element i of lane (l32, gq) in M-tile mt: query row
-        // 32mt + 8(i/4) + 4gq + i%4, key kw0 + l32.  A mixed tile first sets
-        // the scores of invisible pairs to -inf (P = 0, so dS = 0), so the
-        // exponentials below run without a branch.
-        if (cls == 2) {
-          const int key = kw0 + l32;
+        // P = e^{x - L_new}; dS = P (dP - Delta).  Element i of lane (l32,
+        // gq) in M-tile mt: query row q0 + 32mt + 8(i/4) + 4gq + i%4, key
+        // kw0 + l32.  In a mixed tile an invisible pair gets P = 0 (so dS =
+        // 0): with d = row - key, the pair is visible iff 0 <= d < hi, where
+        // hi folds the window (unless the key is a kept first token) and the
+        // sample end; one unsigned compare and a select per element.
+        auto exps = [&](auto MASKED) {
+          constexpr bool masked = decltype(MASKED)::value;
+          int dbase = 0;
+          uint32_t hi = 0u;
+          if constexpr (masked) {
+            const int key = kw0 + l32;
+            dbase = q0 + 4 * gq - key;
+            const int lo = (p.window <= 0 || key < p.n_sink) ? 0x7fffffff : p.window;
+            hi = static_cast<uint32_t>(max(0, min(lo, L - key)));
+          }
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int qi = q0 + 32 * mt + 8 * (i >> 2) + 4 * gq + (i & 3);
-              if (!(qi < L && key_visible(qi, key, p.n_sink, p.window))) sacc[mt][i] = -kInf;
-            }
-        }
-        // P = e^{x - L_new}; dS = P (dP - Delta).
+            for (int u = 0; u < 4; ++u) {
+              const int r0 = 32 * mt + 8 * u + 4 * gq;
+              const f32x4 lv = *reinterpret_cast<const f32x4*>(&lbuf[buf][r0]);
+              const f32x4 dv = *reinterpret_cast<const f32x4*>(&dbuf[buf][r0]);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r0 = 32 * mt + 8 * u + 4 * gq;
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lbuf[buf][r0]);
-            const f32x4 dv = *reinterpret_cast<const f32x4*>(&dbuf[buf][r0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * u + e;
-              const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
-              sacc[mt][i] = pe;
-              pacc[mt][i] = pe * (pacc[mt][i] - dv[e]);
+              for (int e = 0; e < 4; ++e) {
+                const int i = 4 * u + e;
+                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
+                if constexpr (masked)
+                  pe = static_cast<uint32_t>(dbase + 32 * mt + 8 * u + e) < hi ? pe : 0.f;
+                sacc[mt][i] = pe;
+                pacc[mt][i] = pe * (pacc[mt][i] - dv[e]);
+              }
             }
           }
-        }
+        };
+        if (cls == 2) exps(std::true_type{});
+        else exps(std::false_type{});
         // dV += P^T dO and dK += dS^T Q: N = dims (4 tiles), K = 64 query rows.
         bf16x8 pa[4], da[4];
 #pragma unroll
