@@ -127,20 +127,38 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
         }
       }
       // dS^T = P^T (dP^T - Delta); element i of lane (l32, gq) in M-tile mt is
-      // key k0 + 32mt + 8(i/4) + 4gq + i%4, query qi.  A mixed tile first sets
-      // the scores of invisible pairs to -inf, so the exponentials run without
-      // a branch.
+      // key k0 + 4gq + dk with dk = 32mt + 8(i/4) + i%4, query qi.  A mixed
+      // tile first sets the scores of invisible pairs to -inf, so the
+      // exponentials run without a branch.  Visible iff dk <= a (causal) and,
+      // with a window, wb < dk (inside it) or dk < cs (a kept first token);
+      // a, wb, cs per lane, one or two compares and a select per element.
       if (cls == 2) {
-        const int d = qi - k0;
-        const int lo = p.window > 0 ? d - p.window : -(1 << 30);
-        const int sk = p.window > 0 ? p.n_sink - k0 : -(1 << 30);
+        const int kb = k0 + 4 * gq;
+        const int a = qi - kb;
+        // a window longer than qi + 1 keys, or none, covers the same keys as
+        // qi + 1 (all causal keys)
+        const int wlen = p.window > 0 ? min(p.window, qi + 1) : qi + 1;
+        const int wb = a - wlen;
+        const uint32_t span = static_cast<uint32_t>(wlen);
+        if (p.window <= 0 || k0 >= p.n_sink) {       // uniform: no kept token here
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rel = mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
-            if (!(rel <= d && (rel > lo || rel < sk))) sacc[mt][i] = -kInf;
-          }
+            for (int i = 0; i < 16; ++i) {
+              const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
+              sacc[mt][i] = static_cast<uint32_t>(dk - wb - 1) < span ? sacc[mt][i] : -kInf;
+            }
+        } else {
+          const int cs = min(p.n_sink - kb, a + 1);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
+              const bool vis = static_cast<uint32_t>(dk - wb - 1) < span || dk < cs;
+              sacc[mt][i] = vis ? sacc[mt][i] : -kInf;
+            }
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)

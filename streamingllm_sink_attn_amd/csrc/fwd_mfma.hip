@@ -180,16 +180,37 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     }
   };
   // Element mask of a mixed tile: element i of M-tile mt is key
-  // k0 + 32mt + 8(i/4) + 4gq + i%4.
+  // kb + dk with kb = k0 + 4gq and dk = 32mt + 8(i/4) + i%4 fixed per
+  // element.  The pair is visible iff dk <= a (causal) and, with a window,
+  // dk > wb (inside the window) or dk < cs (a kept first token), with a, wb,
+  // cs per lane: one or two compares and a select per element.
   auto mask = [&](int kt, f32x16 (&s)[2]) {
-    const int k0 = kt * BN;
+    const int kb = kt * BN + 4 * gq;
+    const int a = qi - kb;
+    // a window longer than qi + 1 keys, or none, covers the same keys as
+    // qi + 1 (all causal keys): visible iff a - wlen < dk <= a
+    const int wlen = p.window > 0 ? min(p.window, qi + 1) : qi + 1;
+    const int wb = a - wlen;
+    const uint32_t span = static_cast<uint32_t>(wlen);
+    if (p.window <= 0 || kt * BN >= p.n_sink) {      // uniform: no kept token here
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + mt * 32 + 8 * (i >> 2) + 4 * gq + (i & 3);
-        if (!key_visible(qi, key, p.n_sink, p.window)) s[mt][i] = -kInf;
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
+          s[mt][i] = static_cast<uint32_t>(dk - wb - 1) < span ? s[mt][i] : -kInf;
+        }
+    } else {
+      const int cs = min(p.n_sink - kb, a + 1);      // kept first tokens: dk < cs
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
+          const bool vis = static_cast<uint32_t>(dk - wb - 1) < span || dk < cs;
+          s[mt][i] = vis ? s[mt][i] : -kInf;
+        }
+    }
   };
   // Row max of a tile and the lazy rescale to a new base of O, l and the
   // not yet accumulated probabilities pend (which share the old base).
