@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(Prefill p, const vo
         ps = 0.f;
       }
       w.delta[row] = acc;
-      w.lnew[row] = lnew;
+      w.lnew[row] = lnew * kLog2e;         // kept in log2 units for exp2
       w.dsink_terms[row] = -acc * ps;
     }
   }

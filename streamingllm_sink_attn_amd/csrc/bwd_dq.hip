@@ -78,7 +78,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
                "v"(qf[6]), "v"(qf[7]));
   asm volatile("" ::"v"(dof[0]), "v"(dof[1]), "v"(dof[2]), "v"(dof[3]), "v"(dof[4]), "v"(dof[5]),
                "v"(dof[6]), "v"(dof[7]), "v"(Lq), "v"(Dq));
-  const float lb = Lq * kLog2e;
+  const float lb = Lq;                               // L_new in log2 units
 
   Sched sc = make_sched(p, L, qoff, g, p0, p1, bitmap);
 

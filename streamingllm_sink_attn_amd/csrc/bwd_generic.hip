@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64) void bwd_generic_kernel(Prefill p, const void* 
       dot += __shfl_xor(dot, off);
       dpv += __shfl_xor(dpv, off);
     }
-    const float pj = __expf(dot * p.scale - lnew);
+    const float pj = exp2f(dot * p.scale * kLog2e - lnew);   // lnew in log2 units
     const float ds = pj * (dpv - delta);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

@@ -367,9 +367,9 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
       if (cls != 0) {
         const lds_char* qs = (const lds_char*)(qbuf[buf]);
         const lds_char* dos = (const lds_char*)(dobuf[buf]);
-        // P = e^{x - L_new}; dS = P (dP - Delta).  Element i of lane (l32,
-        // gq) in M-tile mt: query row q0 + 32mt + 8(i/4) + 4gq + i%4, key
-        // kw0 + l32.  In a mixed tile an invisible pair gets P = 0 (so dS =
+        // P = e^{x - L_new} (L_new staged in log2 units); dS = P (dP - Delta).
+        // Element i of lane (l32, gq) in M-tile mt: query row q0 + 32mt +
+        // 8(i/4) + 4gq + i%4, key kw0 + l32.  In a mixed tile an invisible pair gets P = 0 (so dS =
         // 0): with d = row - key, the pair is visible iff 0 <= d < hi, where
         // hi folds the window (unless the key is a kept first token) and the
         // sample end; one unsigned compare and a select per element.
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int i = 4 * u + e;
-                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e] * kLog2e));
+                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c_l2, -lv[e]));
                 if constexpr (masked)
                   pe = static_cast<uint32_t>(dbase + 32 * mt + 8 * u + e) < hi ? pe : 0.f;
                 sacc[mt][i] = pe;

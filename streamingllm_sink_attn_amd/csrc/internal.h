@@ -26,7 +26,7 @@ struct Prefill {
 // Backward workspace carve-up (float32 unless noted).
 struct BwdWork {
   float* delta;      // [T, Hq]  rowsum(dO * O)
-  float* lnew;       // [T, Hq]  log(Z + e^a) (or L_orig; +inf for empty rows without a sink)
+  float* lnew;       // [T, Hq]  log2(e) * log(Z + e^a) (or of L_orig; +inf for empty rows without a sink)
   float* dsink_terms;// [T, Hq]  -Delta * p_sink per row
   float* dsink_part; // [ceil(T/64), Hq] per-slab partial sums of the terms
   float* dq_acc;     // [T, Hq, D]  (MFMA path) accumulated dQ
