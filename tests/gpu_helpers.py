@@ -9,10 +9,14 @@ from streamingllm_sink_attn_amd import workloads as W
 
 DEV = "cuda"
 
-# bf16 inputs, float32 accumulation
-TOL_BF16 = dict(o_max=2e-2, o_mean=2e-3, lse=1e-3, s=1e-3, grad=5e-2, dsink_rel=1e-2)
+# bf16 inputs, float32 accumulation.  Gradients are stored in bf16: rounding
+# a value x to bf16 alone moves it by up to half an ulp, 2^-8 |x| at most, which
+# passes 5e-2 once |x| >= 16 (a kept first token's dV sums every row of the
+# sample); the absolute bound applies on top of that representation error.
+TOL_BF16 = dict(o_max=2e-2, o_mean=2e-3, lse=1e-3, s=1e-3, grad=5e-2, grad_out_rel=2.0 ** -8,
+                dsink_rel=1e-2)
 # float32 storage
-TOL_F32 = dict(o_max=1e-4, o_mean=1e-5, lse=1e-4, s=1e-4, grad=1e-4, dsink_rel=1e-4)
+TOL_F32 = dict(o_max=1e-4, o_mean=1e-5, lse=1e-4, s=1e-4, grad=1e-4, grad_out_rel=0.0, dsink_rel=1e-4)
 
 
 def tol_for(dtype):
@@ -80,9 +84,13 @@ def assert_out(got, want, tol, what="O"):
 
 def assert_grad(got, want, tol, what):
     got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    err = float(np.max(np.abs(got - want))) if got.size else 0.0
-    assert err <= tol["grad"], f"{what}: max abs err {err:.3e} > {tol['grad']}"
+    # error beyond the output type's own rounding of the exact value
+    err = np.abs(got - want) - tol["grad_out_rel"] * np.abs(want)
+    worst = float(np.max(err)) if got.size else 0.0
+    assert worst <= tol["grad"], (f"{what}: max abs err beyond bf16 rounding {worst:.3e} > {tol['grad']}"
+                                  f" (raw max abs err {float(np.max(np.abs(got - want))):.3e})")
 
 
 def assert_dsink(got, want, tol):

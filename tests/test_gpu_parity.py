@@ -53,6 +53,10 @@ FWD_CASES = {
     "window_bigsink": dict(lengths=(420,), hq=4, hkv=1, n_sink=70, window=10),
     "window_wide": dict(lengths=(300, 64), hq=4, hkv=2, n_sink=4, window=1000),
     "window_g2": dict(lengths=(390, 129), hq=4, hkv=2, n_sink=4, window=64),
+    # a window of one key (the diagonal only, plus the kept tokens) and one
+    # far longer than any sample (every causal key): the mask bounds' ends
+    "window_one": dict(lengths=(200, 65), hq=4, hkv=1, n_sink=4, window=1),
+    "window_huge": dict(lengths=(300, 70), hq=4, hkv=2, n_sink=4, window=2 ** 30),
     "blocks_g4": dict(lengths=(700, 130), hq=8, hkv=2, block_lists=dict(n_random=3)),
     "blocks_g1": dict(lengths=(513,), hq=2, hkv=2, block_lists=dict(n_random=2)),
     "blocks_window": dict(lengths=(640,), hq=4, hkv=1, n_sink=4, window=150,
@@ -120,7 +124,7 @@ def test_fwd_dynamic_range_example():
 # ---------------------------------------------------------------------------
 
 VISIT_CASES = ["dense_g4", "dense_g2", "dense_g1", "window_sink4", "window_bigsink", "window_g2",
-               "blocks_g4", "blocks_g1", "blocks_window", "blocks_nodiag"]
+               "window_one", "window_huge", "blocks_g4", "blocks_g1", "blocks_window", "blocks_nodiag"]
 
 
 @pytest.mark.parametrize("name", VISIT_CASES)
@@ -161,7 +165,9 @@ def test_q_zero_counts_closed_form():
 # ---------------------------------------------------------------------------
 
 BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "blocks_nodiag",
-             "d64_generic", "dense_g8_long", "window_split", "blocks_split", "dense_g1", "window_g2"]
+             "d64_generic", "dense_g8_long", "window_split", "blocks_split", "dense_g1", "window_g2",
+             "window_bigsink", "window_nosinktok", "window_wide", "window_one", "window_huge",
+             "blocks_window"]
 
 
 @pytest.mark.parametrize("name", BWD_CASES)
