@@ -11,6 +11,8 @@
 // with one query per lane column, so L_new and Delta are per-lane scalars;
 // dS^T in bf16 is directly the B operand of dQ^T += K^T dS^T, whose K^T
 // operand comes from the staged K tile through ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "qmajor.cuh"
 
 namespace sa {
@@ -127,46 +129,42 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
         }
       }
       // dS^T = P^T (dP^T - Delta); element i of lane (l32, gq) in M-tile mt is
-      // key k0 + 4gq + dk with dk = 32mt + 8(i/4) + i%4, query qi.  A mixed
-      // tile first sets the scores of invisible pairs to -inf, so the
-      // exponentials run without a branch.  Visible iff dk <= a (causal) and,
-      // with a window, wb < dk (inside it) or dk < cs (a kept first token);
-      // a, wb, cs per lane, one or two compares and a select per element.
-      if (cls == 2) {
-        const int kb = k0 + 4 * gq;
-        const int a = qi - kb;
-        // a window longer than qi + 1 keys, or none, covers the same keys as
-        // qi + 1 (all causal keys)
-        const int wlen = p.window > 0 ? min(p.window, qi + 1) : qi + 1;
-        const int wb = a - wlen;
-        const uint32_t span = static_cast<uint32_t>(wlen);
-        if (p.window <= 0 || k0 >= p.n_sink) {       // uniform: no kept token here
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
-              sacc[mt][i] = static_cast<uint32_t>(dk - wb - 1) < span ? sacc[mt][i] : -kInf;
-            }
-        } else {
-          const int cs = min(p.n_sink - kb, a + 1);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
-              const bool vis = static_cast<uint32_t>(dk - wb - 1) < span || dk < cs;
-              sacc[mt][i] = vis ? sacc[mt][i] : -kInf;
-            }
+      // key k0 + 4gq + dk with dk = 32mt + 8(i/4) + i%4, query qi.  In a mixed
+      // tile an invisible pair gets P = 0 (so dS = 0): visible iff dk <= a
+      // (causal) and, with a window, wb < dk (inside it) or dk < cs (a kept
+      // first token); a, wb, cs per lane, one or two compares and a select
+      // per element, applied to P.
+      auto exps = [&](auto MASK) {
+        constexpr int mode = decltype(MASK)::value;  // 0: none, 1: range, 2: range or kept token
+        int wb = 0, cs = 0;
+        uint32_t span = 0u;
+        if constexpr (mode > 0) {
+          const int kb = k0 + 4 * gq;
+          const int a = qi - kb;
+          // a window longer than qi + 1 keys, or none, covers the same keys
+          // as qi + 1 (all causal keys)
+          const int wlen = p.window > 0 ? min(p.window, qi + 1) : qi + 1;
+          wb = a - wlen;
+          span = static_cast<uint32_t>(wlen);
+          if constexpr (mode == 2) cs = min(p.n_sink - kb, a + 1);
         }
-      }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c, -lb));
-          pacc[mt][i] = pe * (pacc[mt][i] - Dq);
-        }
+          for (int i = 0; i < 16; ++i) {
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][i], c, -lb));
+            if constexpr (mode > 0) {
+              const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
+              bool vis = static_cast<uint32_t>(dk - wb - 1) < span;
+              if constexpr (mode == 2) vis = vis || dk < cs;
+              pe = vis ? pe : 0.f;
+            }
+            pacc[mt][i] = pe * (pacc[mt][i] - Dq);
+          }
+      };
+      if (cls != 2) exps(std::integral_constant<int, 0>{});
+      else if (p.window <= 0 || k0 >= p.n_sink) exps(std::integral_constant<int, 1>{});   // uniform
+      else exps(std::integral_constant<int, 2>{});
       // dQ^T += K^T dS^T : M = dims (4 tiles), N = 32 queries, K = 64 keys.
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
