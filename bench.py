@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
-    "sha256": "6d5042dd7116b00d1bf2b45f59e98febe59aeec5e700538ca8176d55a8bfc22e",
-    "read_bytes": 224091280,
-    "write_bytes": 142697003,
+    "sha256": "0d5a81d7ed10878c319f6c78b192f5ef7908ad30e456fa9fb21d63422187f387",
+    "read_bytes": 220573554,
+    "write_bytes": 142826549,
 }
 
 
