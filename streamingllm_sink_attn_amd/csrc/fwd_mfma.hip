@@ -20,11 +20,12 @@
 //     registers plus one v_permlane32_swap between the lane halves.  The same
 //     registers, converted to bf16, are the B operand of O^T += V^T P^T; the
 //     V^T operand comes from the staged V tile by ds_read_b64_tr_b16.
-//   * Software pipeline: the scores of tile j+1 are computed in the same
-//     basic block as the exponentials of tile j, and O += V P of tile j next
-//     to the mask and max of tile j+1, so the matrix core and the vector ALU
-//     work at the same time.  K runs one tile ahead of V: K and V each have
-//     two LDS buffers.
+//   * Software pipeline: a step forms the scores of tile j+1 (K fragments
+//     read two MFMAs ahead), masks them and takes their row max, then runs
+//     O += V P of tile j on the matrix core interleaved with the
+//     exponentials of tile j+1 on the vector ALU; the two wavefronts of a
+//     SIMD overlap one another's phases.  K runs one tile ahead of V: K and
+//     V each have two LDS buffers.
 //   * Online softmax with lazy rescaling: the exponent base only moves when a
 //     row's max grows by more than 2^8 (P <= 256), which is exact because O
 //     and l always share the same base.
