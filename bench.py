@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
-    "sha256": "0d5a81d7ed10878c319f6c78b192f5ef7908ad30e456fa9fb21d63422187f387",
+    "sha256": "81cc6c327959c75500e8ad9a4043fdb3c5998f75e540ef829a4f9091385c891b",
     "read_bytes": 220573554,
     "write_bytes": 142826549,
 }
