@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
-    "sha256": "81cc6c327959c75500e8ad9a4043fdb3c5998f75e540ef829a4f9091385c891b",
+    "sha256": "5002a22bd5f9b49f38c2eeb974a5f5df49dcecdc09bc90aa190d51410c0321bc",
     "read_bytes": 220573554,
     "write_bytes": 142826549,
 }

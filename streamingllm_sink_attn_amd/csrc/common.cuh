@@ -74,13 +74,6 @@ __device__ __forceinline__ bool key_visible(int i, int j, int n_sink, int window
   return j <= i && (window <= 0 || j < n_sink || i - j < window);
 }
 
-// Whether KV block kb appears in a block_indices row (duplicates allowed).
-__device__ __forceinline__ bool row_selects(const int32_t* row, int width, int kb) {
-  for (int e = 0; e < width; ++e)
-    if (row[e] == kb) return true;
-  return false;
-}
-
 // Whether entry e of a row is the first occurrence of its block id.
 __device__ __forceinline__ bool first_occurrence(const int32_t* row, int e) {
   int kb = row[e];

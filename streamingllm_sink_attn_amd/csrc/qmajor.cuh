@@ -11,18 +11,17 @@ namespace qm {
 
 constexpr int D = 128;
 constexpr int BN = 64;                 // keys per tile (= block size of block lists)
-constexpr int NW = 4;                  // wavefronts per workgroup
-constexpr int QW = 64;                 // query rows per wavefront
 constexpr int TILE = BN * D;           // bf16 elements of one staged K or V tile (16 KB)
 constexpr int MAX_BITMAP_WORDS = 256;  // block lists: up to 8192 KV blocks per sample
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Geometry: a workgroup holds 4 wavefronts of one KV head g.  With G = Hq/Hkv
-// query heads per KV head, up to 4 of them share the workgroup (GQA packing:
-// each staged K/V tile feeds 4 x 64 query rows); with G = 2 or 1 the
-// wavefronts of a head take consecutive 64-row slabs.
+// Geometry: a workgroup holds nw wavefronts of qw query rows each, all of one
+// KV head g.  With G = Hq/Hkv query heads per KV head, up to nw of them share
+// the workgroup (GQA packing: every staged K/V tile feeds nw x qw query
+// rows); when G has fewer factors of two, the wavefronts of a head take
+// consecutive qw-row slabs.  The forward and dQ kernels use nw = 8, qw = 32.
 // ---------------------------------------------------------------------------
 struct Geo {
   int hw;       // query heads per workgroup
@@ -34,7 +33,7 @@ struct Geo {
 };
 
 // nw wavefronts of qw rows each (nw a power of two, qw dividing 64).
-inline Geo make_geo(const Prefill& p, int nw = NW, int qw = QW) {
+inline Geo make_geo(const Prefill& p, int nw, int qw) {
   Geo g;
   const int G = p.hq / p.hkv;
   g.hw = 1;
@@ -166,24 +165,6 @@ __device__ __forceinline__ int swz16(int row) {
 }
 // Element offset of (row, logical chunk lc).
 __device__ __forceinline__ int at16(int row, int lc) { return row * D + ((lc ^ swz16(row)) << 3); }
-
-// Loads rows [r0, r0 + 64) of a [rows, stride] bf16 tensor into a staged tile
-// with global_load_lds_dwordx4: wavefront `wv` of `nw` issues 16/nw
-// instructions of 4 rows each.  Rows at or past `nvalid` read row nvalid - 1
-// (finite data; the caller masks them).
-__device__ __forceinline__ void load_tile_lds(const uint16_t* base, size_t row_stride, int nvalid,
-                                              uint16_t* lds_tile, int wv, int nw, int lane) {
-  const int per = 16 / nw;
-#pragma unroll 4
-  for (int j = 0; j < per; ++j) {
-    const int blk = wv * per + j;
-    const int row = 4 * blk + (lane >> 4);
-    const int src_row = min(row, nvalid - 1);
-    const int lc = (lane & 15) ^ swz16(row);
-    __builtin_amdgcn_global_load_lds(base + static_cast<size_t>(src_row) * row_stride + lc * 8,
-                                     lds_tile + 4 * blk * D, 16, 0, 0);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Direct-to-LDS buffer loads issued from asm blocks.  With the compiler's own
