@@ -132,14 +132,26 @@ __global__ __launch_bounds__(256) void split_tiles_kernel(Prefill p, BwdWork w, 
   const int t0 = p.cu[t.b];
   const int L = p.cu[t.b + 1] - t0;
   const int rows = min(BN, L - t.kt * BN);
-  for (int e = threadIdx.x; e < rows * D; e += blockDim.x) {
-    const size_t o = (static_cast<size_t>(t0 + t.kt * BN + e / D) * p.hkv + t.g) * D + e % D;
+  // 8 consecutive dims per thread and step: two 16-byte float32 accesses and
+  // one 16-byte bf16 store per tensor.
+  for (int c = threadIdx.x; c < rows * (D / 8); c += blockDim.x) {
+    const int r = c / (D / 8), d0 = (c % (D / 8)) * 8;
+    const size_t o = (static_cast<size_t>(t0 + t.kt * BN + r) * p.hkv + t.g) * D + d0;
     if (kConvert) {
-      dK[o] = f32_to_bf16(w.dk_acc[o]);
-      dV[o] = f32_to_bf16(w.dv_acc[o]);
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(w.dk_acc + o);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(w.dk_acc + o + 4);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(w.dv_acc + o);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(w.dv_acc + o + 4);
+      *reinterpret_cast<u32x4*>(dK + o) = u32x4{pack_bf16x2(k0[0], k0[1]), pack_bf16x2(k0[2], k0[3]),
+                                                pack_bf16x2(k1[0], k1[1]), pack_bf16x2(k1[2], k1[3])};
+      *reinterpret_cast<u32x4*>(dV + o) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                                pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
     } else {
-      w.dk_acc[o] = 0.f;
-      w.dv_acc[o] = 0.f;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(w.dk_acc + o) = z;
+      *reinterpret_cast<f32x4*>(w.dk_acc + o + 4) = z;
+      *reinterpret_cast<f32x4*>(w.dv_acc + o) = z;
+      *reinterpret_cast<f32x4*>(w.dv_acc + o + 4) = z;
     }
   }
 }
