@@ -167,7 +167,7 @@ def test_q_zero_counts_closed_form():
 BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "blocks_nodiag",
              "d64_generic", "dense_g8_long", "window_split", "blocks_split", "dense_g1", "window_g2",
              "window_bigsink", "window_nosinktok", "window_wide", "window_one", "window_huge",
-             "blocks_window"]
+             "blocks_window", "dense_g3", "dense_g8", "stress_sink", "blocks_g1"]
 
 
 @pytest.mark.parametrize("name", BWD_CASES)
