@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FWD_TRAFFIC = {
     "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
     "sha256": "5002a22bd5f9b49f38c2eeb974a5f5df49dcecdc09bc90aa190d51410c0321bc",
-    "read_bytes": 220573554,
-    "write_bytes": 142826549,
+    "read_bytes": 224011061,
+    "write_bytes": 142883616,
 }
 
 
