@@ -48,6 +48,12 @@ FWD_CASES = {
     "dense_g2": dict(lengths=(300, 5), hq=4, hkv=2),
     "dense_g8": dict(lengths=(190,), hq=16, hkv=2),
     "dense_g3": dict(lengths=(150, 70), hq=6, hkv=2),
+    # workgroup geometry: 8 heads per workgroup and two head groups per KV
+    # head (G=16), one head of eight 32-row wavefronts (G=5), three head
+    # groups of four heads (G=12)
+    "dense_g16": dict(lengths=(140, 33), hq=32, hkv=2),
+    "dense_g5": dict(lengths=(300,), hq=5, hkv=1),
+    "window_g12": dict(lengths=(260, 90), hq=12, hkv=1, n_sink=4, window=70),
     "window_sink4": dict(lengths=(400, 77, 260), hq=8, hkv=2, n_sink=4, window=100),
     "window_nosinktok": dict(lengths=(333,), hq=4, hkv=1, n_sink=0, window=50),
     "window_bigsink": dict(lengths=(420,), hq=4, hkv=1, n_sink=70, window=10),
@@ -167,7 +173,8 @@ def test_q_zero_counts_closed_form():
 BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "blocks_nodiag",
              "d64_generic", "dense_g8_long", "window_split", "blocks_split", "dense_g1", "window_g2",
              "window_bigsink", "window_nosinktok", "window_wide", "window_one", "window_huge",
-             "blocks_window", "dense_g3", "dense_g8", "stress_sink", "blocks_g1"]
+             "blocks_window", "dense_g3", "dense_g8", "stress_sink", "blocks_g1", "dense_g16", "dense_g5",
+             "window_g12"]
 
 
 @pytest.mark.parametrize("name", BWD_CASES)
