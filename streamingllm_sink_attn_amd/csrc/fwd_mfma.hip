@@ -83,7 +83,9 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   const int p1 = min(L, p0 + geo.P);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // wavefront index as a scalar, so per-wavefront tile decisions are
+  // uniform branches rather than exec-masked regions
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int gq = lane >> 5;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
   const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
   DmaTiles<FNW> ld;
-  ld.init(__builtin_amdgcn_readfirstlane(w), lane, kvs);
+  ld.init(w, lane, kvs);
   const uint32_t kbuf0 = lds_address(&kbuf[0][0]), vbuf0 = lds_address(&vbuf[0][0]);
   auto issue_k = [&](int kt, int st) {
     const int k0 = kt * BN;
@@ -215,13 +217,13 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   };
   // Row max of a tile and the lazy rescale to a new base of O, l and the
   // not yet accumulated probabilities pend (which share the old base).
-  auto update_max = [&](const f32x16 (&s)[2], bf16x8 (&pend)[4]) {
+  auto update_max = [&](const f32x16 (&s)[2], bool dead, bf16x8 (&pend)[4]) {
     float m0 = -kInf;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) m0 = __builtin_fmaxf(m0, s[mt][i]);
-    m0 = xhalf_max(m0);
+    m0 = dead ? -kInf : xhalf_max(m0);
     if (__ballot(m0 > mrun + thr) != 0) {
       const float mnew = __builtin_fmaxf(mrun, m0);
       const float f = (mrun == -kInf) ? 0.f : __builtin_amdgcn_exp2f((mrun - mnew) * c);
@@ -241,9 +243,8 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       mrun = mnew;
     }
   };
-  // P = 2^(c x - c m) in bf16 as four k-steps, l += sum P.
-  auto probs = [&](f32x16 (&s)[2], bf16x8 (&pf)[4]) {
-    const float mb = (mrun == -kInf) ? 0.f : mrun * c;
+  // P = 2^(c x - mb) in bf16 as four k-steps, l += sum P.
+  auto probs = [&](f32x16 (&s)[2], float mb, bf16x8 (&pf)[4]) {
     float ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -270,20 +271,18 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       }
   };
 
-  // A tile this wavefront does not see gets scores of -inf: its P is 0 and
-  // it changes nothing, so the steady state needs no per-wavefront branch.
-  auto kill = [&](f32x16 (&s)[2]) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[mt][i] = -kInf;
-  };
-  // Mask (or kill) the scores of tile kt and move the base if needed.
+  // Mask the scores of tile kt if it is mixed, move the base if needed and
+  // return the exponent base c m for its P.  A tile this wavefront does not
+  // see leaves the max alone and takes an infinite base, so its P is exactly
+  // 0 and its scores need no rewrite.
   auto finish_scores = [&](int kt, f32x16 (&s)[2], bf16x8 (&pend)[4]) {
     const int cls = tile_class(kt);
-    if (cls == 0) kill(s);
-    else if (cls == 2) mask(kt, s);
-    update_max(s, pend);
+    if (cls == 2) mask(kt, s);
+    update_max(s, cls == 0, pend);
+    float mb = (mrun == -kInf) ? 0.f : mrun * c;
+    if (cls == 0) mb = kInf;
+    asm volatile("" : "+v"(mb));                     // settled here, not inside the P V loop
+    return mb;
   };
 
   int t_cur = sc.next();
@@ -291,7 +290,9 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     int t_nx = sc.next();
     issue_k(t_cur, 0);
     issue_v(t_cur, 0);
-    if (t_nx >= 0) issue_k(t_nx, 1);
+    // K buffer 1 always holds a real tile: the last step forms (and
+    // discards) the scores of a tile that does not exist from it.
+    issue_k(t_nx >= 0 ? t_nx : t_cur, 1);
     wait_bar<0>();
     bf16x8 pf[4];                                    // P of tile "cur" (bf16)
 #pragma unroll
@@ -299,39 +300,38 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     {
       f32x16 s0[2];
       scores(std::integral_constant<int, 0>{}, s0);
-      finish_scores(t_cur, s0, pf);
-      probs(s0, pf);
+      const float mb = finish_scores(t_cur, s0, pf);
+      probs(s0, mb, pf);
     }
     wait_bar<0>();
 
     // One pipeline step: P of tile "cur" is in pf and its V in V buffer ST;
-    // K of tile "nx" is in K buffer ST^1.  K of the tile after next goes to K
+    // K of "nx" is in K buffer ST^1.  K of the tile after next goes to K
     // buffer ST and V of "nx" to V buffer ST^1.  O += V P of "cur" (matrix
-    // core) is interleaved with the exponentials of "nx" (vector ALU).
+    // core) is interleaved with the exponentials of "nx" (vector ALU).  The
+    // last step has no tile "nx": it forms the scores of whatever K buffer
+    // ST^1 holds and discards them as a tile this wavefront does not see
+    // (P = 0), so every step runs the same code and O needs no merge.
     auto step = [&](auto ST) {
       constexpr int st = decltype(ST)::value;
       const int t_nx2 = sc.next();
       if (t_nx2 >= 0) issue_k(t_nx2, st);
-      if (t_nx >= 0) {                               // uniform over the workgroup
-        issue_v(t_nx, st ^ 1);
-        f32x16 s_nx[2];
-        scores(std::integral_constant<int, st ^ 1>{}, s_nx);
-        finish_scores(t_nx, s_nx, pf);
-        bf16x8 pn[4];
-        pv(std::integral_constant<int, st>{}, pf);
-        probs(s_nx, pn);
+      if (t_nx >= 0) issue_v(t_nx, st ^ 1);
+      f32x16 s_nx[2];
+      scores(std::integral_constant<int, st ^ 1>{}, s_nx);
+      const float mb = finish_scores(t_nx, s_nx, pf);
+      bf16x8 pn[4];
+      pv(std::integral_constant<int, st>{}, pf);
+      probs(s_nx, mb, pn);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) pf[cc] = pn[cc];
-      } else {
-        pv(std::integral_constant<int, st>{}, pf);
-      }
+      for (int cc = 0; cc < 4; ++cc) pf[cc] = pn[cc];
       // This step's loads landed and no read of the buffers they refill next
       // step is in flight.
       wait_bar<0>();
       t_cur = t_nx;
       t_nx = t_nx2;
     };
-    while (true) {
+    while (true) {                                   // t_cur is uniform over the workgroup
       step(std::integral_constant<int, 0>{});
       if (t_cur < 0) break;
       step(std::integral_constant<int, 1>{});
