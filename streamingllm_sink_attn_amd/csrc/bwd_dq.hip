@@ -40,7 +40,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
   const int p1 = min(L, p0 + geo.P);
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: tile decisions branch uniformly
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int gq = lane >> 5;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
   const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
   const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
   DmaTiles<NWQ> ld;
-  ld.init(__builtin_amdgcn_readfirstlane(wv), lane, kvs);
+  ld.init(wv, lane, kvs);
   const uint32_t kv0 = lds_address(&kv[0][0][0]);
   auto issue = [&](int kt, int st) {
     const int k0 = kt * BN;

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
   __shared__ __attribute__((aligned(16))) uint16_t dobuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float lbuf[2][BM];
   __shared__ __attribute__((aligned(16))) float dbuf[2][BM];
-  __shared__ int qt_tab[kChunk];     // query tile of each iteration of the item
+  __shared__ int qt_tab[kChunk];     // query head and tile of each iteration of the item
   __shared__ int item_sh;
 
   const int tid = threadIdx.x;
@@ -284,9 +284,11 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
                  "v"(vB[6]), "v"(vB[7]));
     // Query tiles of the item's iterations, read from the reverse list once
     // (the loop then issues no vector memory operation besides the DMA).
+    // Entry: (query head within the group) << 16 | query tile.
     for (int j = tid; j < it_end - it_begin; j += 64 * NWK) {
-      const int n = (it_begin + j) % tw.per_head;
-      qt_tab[j] = tw.list ? tw.list[n] : tw.qt_begin + n;
+      const int it = it_begin + j;
+      const int n = it % tw.per_head;
+      qt_tab[j] = ((it / tw.per_head) << 16) | (tw.list ? tw.list[n] : tw.qt_begin + n);
     }
     __syncthreads();
     f32x16 dKacc[4], dVacc[4];
@@ -296,8 +298,9 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
       for (int i = 0; i < 16; ++i) { dKacc[nt][i] = 0.f; dVacc[nt][i] = 0.f; }
 
     auto coord = [&](int it, int* h, int* qt) {
-      *h = g * G + it / tw.per_head;
-      *qt = qt_tab[it - it_begin];
+      const int e = __builtin_amdgcn_readfirstlane(qt_tab[it - it_begin]);   // scalar from here on
+      *h = g * G + (e >> 16);
+      *qt = e & 0xffff;
     };
     // Stage the Q / dO tile and the L_new (wavefront 0) or Delta (wavefront
     // 1) rows of iteration it in buffer buf: direct-to-LDS buffer loads from
