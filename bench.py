@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ("fwd_mfma.hip", "qmajor.cuh", "common.cuh"),
-    "sha256": "5002a22bd5f9b49f38c2eeb974a5f5df49dcecdc09bc90aa190d51410c0321bc",
-    "read_bytes": 224011061,
-    "write_bytes": 142883616,
+    "sha256": "90bd47047c91921f753f379a4b328bc5bd8957fd844f86e930de73bb810d2ec5",
+    "read_bytes": 224956869,
+    "write_bytes": 143003403,
 }
 
 
