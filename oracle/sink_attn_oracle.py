@@ -26,6 +26,10 @@ Backward:
   Delta_ih = sum_d dO_ihd O_ihd                    [Notes] s7, definition of Delta
   dx_ij    = P_ij (<dO_ih, V_jg> - Delta_ih)       [Notes] s8, score gradient
   dsink_h  = -sum_i Delta_ih (1 - s_ih)            [Notes] s7, boxed equation
+Gate statistics:
+  G_ih     = sigma(LSE_not0 - x_i0)                [MoE] s5, vanilla attention
+             (the first token of the sample plays the sink: G = 1 - A_0, s2)
+  Imp_h    = (1/|T|) sum_i G_ih                    [MoE] s4, head importance
 
 Readings where the pages leave a step open (each is listed in the design doc):
   * g(h) = h // (Hq / Hkv): contiguous groups of query heads share a KV head.
@@ -42,6 +46,9 @@ Readings where the pages leave a step open (each is listed in the design doc):
     no sink (s = 1); an empty valid set gives O = 0, lse = -inf and s = 0 with
     a sink (s = 1 without).
   * dsink is a plain sum over every query row of the call, with no mean.
+  * first-token gate: the sink of vanilla attention is the sample's first
+    token; G = 1 when that token is not a valid key of the row (no term to
+    remove), 0 for a row with no valid key at all.
 """
 from __future__ import annotations
 
@@ -49,7 +56,8 @@ import numpy as np
 
 __all__ = [
     "kv_head", "sample_mask", "fwd", "fwd_virtual_key", "bwd", "decode",
-    "fwd_rows", "bwd_rows", "bwd_kv_rows", "logsumexp_rows",
+    "fwd_rows", "bwd_rows", "bwd_kv_rows", "logsumexp_rows", "first_token_gate",
+    "first_token_gate_rows", "head_importance",
 ]
 
 
@@ -194,6 +202,56 @@ def fwd_virtual_key(q, k, v, cu_seqlens, scale, n_sink=0, window=0, block_indice
                 o[t0:t1, h, :] = p[:, :L] @ v[t0:t1, g, :]
                 s_out[t0:t1, h] = p[:, :L].sum(axis=1) if a is not None else 1.0
     return o, s_out
+
+
+def first_token_gate(q, k, cu_seqlens, scale, n_sink=0, window=0, block_indices=None,
+                     block_size=64):
+    """Vanilla-attention gate G [T,Hq] in float64 ([MoE] s5, vanilla form).
+
+    The sample's first token is the sink of vanilla attention; its share of
+    the softmax is taken out through the log-sum-exp of the other valid keys:
+    G = sigma(LSE_not0 - x_i0), where x_i0 = alpha <q_i, k_0> and LSE_not0 is
+    the log-sum-exp over the valid keys other than the first.  By [MoE] s2 this
+    is 1 - A_0, the output scale the first token imposes when its value is 0.
+    A row whose first key is not valid gets 1; a row with no valid key gets 0.
+    """
+    q, k = _as64(q), _as64(k)
+    T, hq, _ = q.shape
+    hkv = k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    qoff = _q_block_offsets(cu, block_size)
+    gate = np.zeros((T, hq))
+    for b in range(len(cu) - 1):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        L = t1 - t0
+        if L == 0:
+            continue
+        for g in range(hkv):
+            M = sample_mask(L, n_sink, window, _blocks_of(block_indices, qoff, b, g), block_size)
+            for h in range(hq):
+                if kv_head(h, hq, hkv) != g:
+                    continue
+                x = scale * (q[t0:t1, h, :] @ k[t0:t1, g, :].T)
+                x = np.where(M, x, -np.inf)
+                x0 = x[:, 0].copy()                          # first-token score (-inf if not valid)
+                rest = x.copy()
+                rest[:, 0] = -np.inf
+                lse_not0 = logsumexp_rows(rest)
+                empty = ~np.isfinite(x0) & ~np.isfinite(lse_not0)
+                with np.errstate(over="ignore", invalid="ignore"):
+                    z = np.where(empty, 0.0, lse_not0 - np.where(np.isfinite(x0), x0, -np.inf))
+                    G = 1.0 / (1.0 + np.exp(-z))             # sigma(LSE_not0 - x_i0)
+                gate[t0:t1, h] = np.where(empty, 0.0, G)
+    return gate
+
+
+def head_importance(gate):
+    """Imp_h = (1/|T|) sum_i G_ih: the mean gate of each head over the rows
+    ([MoE] s4); 0 for no rows."""
+    g = np.asarray(gate, dtype=np.float64)
+    if g.shape[0] == 0:
+        return np.zeros(g.shape[1])
+    return g.sum(axis=0) / g.shape[0]
 
 
 def bwd(q, k, v, cu_seqlens, scale, do, n_sink=0, window=0, block_indices=None,
@@ -346,6 +404,33 @@ def fwd_rows(q, k, v, cu_seqlens, scale, rows, n_sink=0, window=0, block_indices
         lses.append(lorig)
         ss.append(s)
     return np.array(outs), np.array(lses), np.array(ss)
+
+
+def first_token_gate_rows(q, k, cu_seqlens, scale, rows, n_sink=0, window=0, block_indices=None,
+                          block_size=64):
+    """First-token gate ([MoE] s5) for the given (token, head) pairs only [n]:
+    sigma(LSE_not0 - x_i0) over the row's valid keys, 1 without a valid first
+    key, 0 without any valid key (the same definition as first_token_gate)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    qoff = _q_block_offsets(cu, block_size)
+    hq, hkv = q.shape[1], k.shape[1]
+    out = []
+    for t, h in rows:
+        g = kv_head(int(h), hq, hkv)
+        keys, b = _row_keys(cu, qoff, int(t), g, n_sink, window, block_indices, block_size)
+        if len(keys) == 0:
+            out.append(0.0)
+            continue
+        x = scale * (np.asarray(k[keys, g, :], dtype=np.float64)
+                     @ np.asarray(q[int(t), int(h), :], dtype=np.float64))
+        first = keys == cu[b]
+        if not np.any(first):
+            out.append(1.0)
+            continue
+        lse_not0 = logsumexp_rows(x[~first][None, :])[0]
+        with np.errstate(over="ignore"):
+            out.append(1.0 / (1.0 + np.exp(-(lse_not0 - x[first][0]))))
+    return np.array(out)
 
 
 def bwd_rows(q, k, v, cu_seqlens, scale, do, rows, n_sink=0, window=0, block_indices=None,

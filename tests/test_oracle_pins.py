@@ -445,6 +445,98 @@ def test_row_evaluators_match_full():
 
 
 # ---------------------------------------------------------------------------
+# First-token gate and head importance ("Paper notes: Attention Sink and the
+# native MoE in attention layers", s2, s4, s5)
+# ---------------------------------------------------------------------------
+
+def test_first_token_gate_worked_example():
+    """Section-1 weights [0.75, 0.25]: the first token takes 0.75, so the
+    vanilla gate G = 1 - A_0 is 0.25; query 0 sees only the first token (0)."""
+    q, k, _, cu = _two_key_case()
+    g = oracle.first_token_gate(q, k, cu, 1.0)
+    w = GOLDEN["output_weighted_sum"]["weights"]
+    assert abs(g[1, 0] - (1.0 - w[0])) < 1e-15
+    assert g[0, 0] == 0.0
+    assert abs(oracle.head_importance(g)[0] - (1.0 - w[0]) / 2) < 1e-15
+
+
+def _first_token_probe(rng, mask, hq=4, hkv=2, D=6, lengths=(37, 70, 1)):
+    """V one-hot on each sample's first token: the forward's output column 0
+    is then the attention weight A_0 of every row (no sink)."""
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q = _rand(rng, T, hq, D)
+    k = _rand(rng, T, hkv, D)
+    v = np.zeros((T, hkv, D))
+    v[cu[:-1], :, 0] = 1.0
+    o, lse, _ = oracle.fwd(q, k, v, cu, 0.4, **mask)
+    return q, k, cu, o[:, :, 0], lse
+
+
+@pytest.mark.parametrize("mask", [dict(), dict(n_sink=3, window=9), dict(n_sink=0, window=5),
+                                  "blocks"])
+def test_first_token_gate_is_one_minus_first_token_weight(mask):
+    """The LSE form sigma(LSE_not0 - x_0) of s5 equals 1 - A_0 of s2, A_0 read
+    through the forward's P V with a one-hot first value."""
+    rng = np.random.default_rng(21)
+    if mask == "blocks":
+        lengths = (130, 64)
+        nqb = 3 + 1
+        bi = np.full((nqb, 2, 2), -1, dtype=np.int32)
+        bi[0, :, 0] = 0
+        bi[1, 0, :] = [1, 0]          # head 0: both blocks; head 1: block 1 only (no first key)
+        bi[1, 1, 0] = 1
+        bi[2, :, 0] = 2               # diagonal only: no first key
+        bi[3, :, 0] = 0
+        mask = dict(block_indices=bi)
+        q, k, cu, a0, lse = _first_token_probe(rng, mask, lengths=lengths)
+    else:
+        q, k, cu, a0, lse = _first_token_probe(rng, mask)
+    g = oracle.first_token_gate(q, k, cu, 0.4, **mask)
+    valid = np.isfinite(lse)
+    np.testing.assert_allclose(g[valid], 1.0 - a0[valid], rtol=0, atol=1e-12)
+    assert np.all(g[~valid] == 0.0)
+    if mask.get("window", 0) > 0 and mask.get("n_sink", 0) == 0:
+        # rows past the window cannot see the first token: G = 1 exactly
+        L0 = 37
+        assert np.all(g[5:L0] == 1.0)
+
+
+def test_implicit_gate_identity():
+    """s2: with a zero first value, vanilla attention equals G times the
+    attention over the other tokens (the sample with its first token removed)."""
+    rng = np.random.default_rng(22)
+    L, hq, hkv, D = 29, 4, 2, 8
+    q, k, v = _rand(rng, L, hq, D), _rand(rng, L, hkv, D), _rand(rng, L, hkv, D)
+    v0 = v.copy()
+    v0[0] = 0.0
+    o, _, _ = oracle.fwd(q, k, v0, [0, L], 0.35)
+    g = oracle.first_token_gate(q, k, [0, L], 0.35)
+    o_rest, _, _ = oracle.fwd(q[1:], k[1:], v[1:], [0, L - 1], 0.35)
+    np.testing.assert_allclose(o[1:], g[1:, :, None] * o_rest, rtol=0, atol=1e-12)
+    assert np.all(o[0] == 0.0) and np.all(g[0] == 0.0)
+
+
+def test_first_token_gate_rows_match_full():
+    rng = np.random.default_rng(23)
+    lengths = (150, 40)
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k = _rand(rng, T, 4, 8), _rand(rng, T, 2, 8)
+    for mask in (dict(), dict(n_sink=2, window=30), dict(n_sink=0, window=30)):
+        full = oracle.first_token_gate(q, k, cu, 0.3, **mask)
+        rows = [(0, 0), (1, 3), (60, 1), (149, 2), (150, 0), (189, 3)]
+        got = oracle.first_token_gate_rows(q, k, cu, 0.3, rows, **mask)
+        np.testing.assert_allclose(got, [full[t, h] for t, h in rows], rtol=0, atol=1e-13)
+
+
+def test_head_importance_is_the_mean_gate():
+    g = np.array([[0.0, 1.0], [0.5, 1.0], [1.0, 0.25]])
+    np.testing.assert_allclose(oracle.head_importance(g), [0.5, 0.75], atol=1e-15)
+    assert np.all(oracle.head_importance(np.zeros((0, 3))) == 0.0)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each must be caught by one of the checks above
 # ---------------------------------------------------------------------------
 
@@ -468,3 +560,10 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert abs(s[1, 0] - 0.2) < 1e-15
     o_bad, _, s_bad = so.fwd(q2, k, v, cu, 0.5, sink=a * 0.5)
     assert abs(s_bad[1, 0] - 0.2) > 0.1
+    # gate with the first token left inside the log-sum-exp: sigma(LSE - x_0)
+    # = 1 / (1 + A_0) instead of 1 - A_0, far from the worked example's 0.25
+    qg, kg, _, cug = _two_key_case()
+    lse_all = math.log(4.0)
+    wrong = 1.0 / (1.0 + math.exp(-(lse_all - math.log(3.0))))
+    right = so.first_token_gate(qg, kg, cug, 1.0)[1, 0]
+    assert abs(right - 0.25) < 1e-15 and abs(wrong - 0.25) > 0.3
