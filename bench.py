@@ -137,6 +137,39 @@ def bench_gqa_prefill(torch, sa, W, steps, warmup):
                 tflops=tflops, wl=wl)
 
 
+def bench_gqa_gated(torch, sa, W, steps, warmup):
+    """The GQA prefill forward with the first-token gate written, and the head
+    importance of that gate.  Timed apart: the plain forward, the gated
+    forward (its overhead is the gate's cost inside the kernel) and one head
+    importance call ([T, Hq] float32 in, [Hq] out)."""
+    wl = W.gqa_prefill()
+    q, k, v = _dev_bf16(wl.q, torch), _dev_bf16(wl.k, torch), _dev_bf16(wl.v, torch)
+    cu = torch.from_numpy(wl.cu_seqlens).cuda()
+    sink = torch.from_numpy(wl.sink).cuda()
+    o = torch.empty_like(q)
+    gate = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    imp = torch.empty(wl.hq, dtype=torch.float32, device="cuda")
+    pairs = _counts_window(wl.lengths, 0, 0) * wl.hq
+    flops = 4.0 * wl.d * pairs
+
+    def plain():
+        sa.fwd(q, k, v, cu, wl.max_seqlen, wl.scale, 0, 0, None, sink, return_s=True, out=o)
+
+    def gated():
+        sa.fwd(q, k, v, cu, wl.max_seqlen, wl.scale, 0, 0, None, sink, return_s=True, out=o,
+               gate0=gate)
+
+    ms_plain, _ = Timer(torch).run(plain, steps, warmup)
+    ms, _ = Timer(torch).run(gated, steps, warmup)
+    ms_imp, _ = Timer(torch).run(lambda: sa.head_importance(gate, out=imp), steps, warmup)
+    return dict(workload="gqa_prefill_fwd_gated", unit="TFLOP/s",
+                value=round(flops / (ms * 1e-3) / 1e12, 2), ms_per_step=round(ms, 4),
+                plain_fwd_ms=round(ms_plain, 4), gate_overhead=round(ms / ms_plain - 1.0, 4),
+                head_importance_ms=round(ms_imp, 4),
+                note="forward with the first-token gate written (FLOPs: the forward's 4*D per "
+                     "valid pair); head importance timed alone")
+
+
 def _fwd_bwd_leg(torch, sa, wl, pairs, name, steps, warmup, cfg):
     """Times one forward + backward per step; FLOPs are 14*D per valid pair
     (4*D forward, 10*D backward), and fwd / bwd are also timed alone."""
@@ -259,9 +292,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: the GPU reaches its steady clocks only after "
+                         "tens of milliseconds of load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks"),
+    ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks", "gated"),
                     default="all",
                     help="headline: only the GQA prefill forward (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -286,7 +321,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     single = {"decode": bench_decode, "streaming": bench_streaming_prefill,
-              "blocks": bench_block_sparse}
+              "blocks": bench_block_sparse, "gated": bench_gqa_gated}
     if args.legs in single:
         print(json.dumps(single[args.legs](torch, sa, W, args.steps, args.warmup)), flush=True)
         return
@@ -313,7 +348,8 @@ def main():
         "roofline": roofline,
     }
     also = []
-    legs = (bench_streaming_prefill, bench_decode, bench_block_sparse) if args.legs == "all" else ()
+    legs = ((bench_streaming_prefill, bench_decode, bench_block_sparse, bench_gqa_gated)
+            if args.legs == "all" else ())
     for fn in legs:
         try:
             also.append(fn(torch, sa, W, args.steps, args.warmup))

@@ -171,6 +171,42 @@ int sink_attn_fwd(const sink_attn_prefill_desc* desc,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward with the first-token gate of vanilla attention.  "Paper notes:
+ * Attention Sink and the native MoE in attention layers" (lvdousha26.github.io)
+ * s2: a sink whose value vector is zero scales the head's output by
+ * G = 1 - A_sink; s5: for vanilla attention, where the sample's first token
+ * plays the sink, that gate comes from the log-sum-exp as
+ * G = sigma(LSE_not0 - x_i0), with no attention matrix stored.
+ *   gate0   output float32 [T, Hq]: the share of the real-token softmax that
+ *           is not on the sample's first key,
+ *             sum_{j valid, j != 0} e^{x_ij} / sum_{j valid} e^{x_ij},
+ *           1 when the first key is not valid for the query, 0 for a query
+ *           with no valid key.  NULL = not written (the call is then
+ *           sink_attn_fwd).  It does not depend on learnable_sink, whose own
+ *           gate sigma(LSE - sink) is s.
+ * Every other argument, output and error as sink_attn_fwd.
+ */
+int sink_attn_fwd_gated(const sink_attn_prefill_desc* desc,
+                        const void* q, const void* k, const void* v,
+                        void* o, float* lse, float* s, float* gate0,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Head importance, "Paper notes: Attention Sink and the native MoE in
+ * attention layers" s4: Imp_h, the mean of a per-row gate over the rows.
+ *   gate       device float32 [rows, num_heads] (s of sink attention, or
+ *              gate0 of sink_attn_fwd_gated).
+ *   imp        output device float32 [num_heads]:
+ *                imp[h] = (1 / rows) sum_r gate[r, h],
+ *              summed in a fixed order (deterministic); 0 when rows == 0.
+ *   workspace  at least sink_attn_head_importance_workspace_size(rows,
+ *              num_heads) bytes (NULL allowed when that is 0).
+ */
+int sink_attn_head_importance(const float* gate, int32_t rows, int32_t num_heads,
+                              float* imp, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Backward.  [Notes] s7 (dsink, Delta) and s8 (sink-aware dQ/dK/dV).
  *   o, lse    the forward's outputs for the same inputs (o is O_new).
  *   dout      upstream gradient dO [T, Hq, D], dtype of q.
@@ -202,6 +238,7 @@ int sink_attn_decode(const sink_attn_decode_desc* desc,
 size_t sink_attn_fwd_workspace_size(const sink_attn_prefill_desc* desc);
 size_t sink_attn_bwd_workspace_size(const sink_attn_prefill_desc* desc);
 size_t sink_attn_decode_workspace_size(const sink_attn_decode_desc* desc);
+size_t sink_attn_head_importance_workspace_size(int32_t rows, int32_t num_heads);
 
 /*
  * Pure host validation of the scalar arguments and pointers of the matching
@@ -221,6 +258,12 @@ int sink_attn_check_decode(const sink_attn_decode_desc* desc,
                            const void* q, const void* k_cache, const void* v_cache,
                            const void* o, const float* lse, const float* s,
                            size_t workspace_bytes);
+int sink_attn_check_fwd_gated(const sink_attn_prefill_desc* desc,
+                              const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const float* s,
+                              const float* gate0, size_t workspace_bytes);
+int sink_attn_check_head_importance(const float* gate, int32_t rows, int32_t num_heads,
+                                    const float* imp, size_t workspace_bytes);
 
 /* Static description of a status code; never NULL. */
 const char* sink_attn_strerror(int status);

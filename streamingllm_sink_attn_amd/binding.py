@@ -70,6 +70,13 @@ _lib = None
 
 _SIGS = {
     "sink_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_fwd_gated": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    ctypes.c_size_t, c_vp]),
+    "sink_attn_head_importance": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_head_importance_workspace_size": (ctypes.c_size_t, [c_i32, c_i32]),
+    "sink_attn_check_fwd_gated": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          ctypes.c_size_t]),
+    "sink_attn_check_head_importance": (c_i32, [c_vp, c_i32, c_i32, c_vp, ctypes.c_size_t]),
     "sink_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               c_vp, ctypes.c_size_t, c_vp]),
     "sink_attn_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
@@ -168,8 +175,13 @@ def _max_seqlen(cu_seqlens: torch.Tensor, max_seqlen: Optional[int]) -> int:
 
 
 def fwd(q, k, v, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,
-        block_indices=None, learnable_sink=None, return_s=True, out=None, stream=None):
-    """Forward.  Returns (o [T,Hq,D], lse [T,Hq] float32 L_orig, s [T,Hq] or None)."""
+        block_indices=None, learnable_sink=None, return_s=True, out=None, stream=None,
+        gate0=None):
+    """Forward.  Returns (o [T,Hq,D], lse [T,Hq] float32 L_orig, s [T,Hq] or None).
+
+    gate0: None, or a float32 [T,Hq] tensor that receives the first-token gate
+    (sink_attn_fwd_gated).
+    """
     _need_cuda(q, k, v, cu_seqlens, block_indices, learnable_sink)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
     desc = prefill_desc(q, k, cu_seqlens, _max_seqlen(cu_seqlens, max_seqlen), scale, n_sink, window,
@@ -181,9 +193,40 @@ def fwd(q, k, v, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, wind
     L = lib()
     ws_bytes = L.sink_attn_fwd_workspace_size(ctypes.byref(desc))
     ws = _workspace(ws_bytes, q.device)
-    _check(L.sink_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
-                           _p(ws), ws_bytes, _stream(stream)))
+    if gate0 is None:
+        _check(L.sink_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
+                               _p(ws), ws_bytes, _stream(stream)))
+    else:
+        _need_cuda(gate0)
+        if gate0.dtype != torch.float32 or tuple(gate0.shape) != (T, hq):
+            raise SinkAttnError(INVALID_ARGUMENT, "gate0 must be float32 [T, Hq]")
+        _check(L.sink_attn_fwd_gated(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
+                                     _p(gate0), _p(ws), ws_bytes, _stream(stream)))
     return o, lse, s
+
+
+def fwd_gated(q, k, v, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,
+              block_indices=None, learnable_sink=None, return_s=True, out=None, stream=None):
+    """Forward plus the first-token gate.  Returns (o, lse, s or None, gate0 [T,Hq] float32)."""
+    gate0 = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    o, lse, s = fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale, n_sink, window, block_indices,
+                    learnable_sink, return_s, out, stream, gate0=gate0)
+    return o, lse, s, gate0
+
+
+def head_importance(gate, out=None, stream=None):
+    """Mean of a per-row gate [rows, H] over the rows: float32 [H] (deterministic)."""
+    _need_cuda(gate)
+    if gate.dtype != torch.float32 or gate.dim() != 2:
+        raise SinkAttnError(INVALID_ARGUMENT, "gate must be float32 [rows, heads]")
+    rows, heads = int(gate.shape[0]), int(gate.shape[1])
+    imp = out if out is not None else torch.empty(heads, dtype=torch.float32, device=gate.device)
+    L = lib()
+    ws_bytes = L.sink_attn_head_importance_workspace_size(rows, heads)
+    ws = _workspace(ws_bytes, gate.device)
+    _check(L.sink_attn_head_importance(_p(gate), rows, heads, _p(imp), _p(ws), ws_bytes,
+                                       _stream(stream)))
+    return imp
 
 
 def bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,

@@ -244,12 +244,14 @@ hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st) 
 // ---------------------------------------------------------------------------
 // Finish: dsink[h] = sum_t terms[t, h] in a fixed order; accumulators -> dtype.
 // ---------------------------------------------------------------------------
-// Two passes, both in a fixed order: per slab of kDsinkRows rows, partial
-// sums of every head (reads are contiguous across the heads of a row), then
-// per head the sum of the slabs' partials.
+// Column sums in two passes, both in a fixed order: per slab of kDsinkRows
+// rows, partial sums of every column (reads are contiguous across the
+// columns of a row), then per column the sum of the slabs' partials, times a
+// scale.  dsink uses them on the per-row terms (scale 1); the head importance
+// on a per-row gate (scale 1 / rows).
 constexpr int kDsinkRows = 64;
 
-__global__ __launch_bounds__(256) void dsink_partial_kernel(const float* __restrict__ terms, int T,
+__global__ __launch_bounds__(256) void column_sum_partial_kernel(const float* __restrict__ terms, int T,
                                                             int hq, float* __restrict__ part) {
   __shared__ float red[256];
   const int t0 = blockIdx.x * kDsinkRows;
@@ -274,8 +276,9 @@ __global__ __launch_bounds__(256) void dsink_partial_kernel(const float* __restr
 
 // One workgroup per head: thread t sums slabs t, t + 256, ... in order, then
 // a fixed tree over the 256 partial sums.
-__global__ __launch_bounds__(256) void dsink_final_kernel(const float* __restrict__ part, int nslab,
-                                                          int hq, float* __restrict__ dsink) {
+__global__ __launch_bounds__(256) void column_sum_final_kernel(const float* __restrict__ part, int nslab,
+                                                               int hq, float scale,
+                                                               float* __restrict__ out) {
   __shared__ float red[256];
   const int h = blockIdx.x;
   float acc = 0.f;
@@ -286,10 +289,21 @@ __global__ __launch_bounds__(256) void dsink_final_kernel(const float* __restric
     if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dsink[h] = red[0];
+  if (threadIdx.x == 0) out[h] = red[0] * scale;
 }
 
 int dsink_slabs(int total) { return (total + kDsinkRows - 1) / kDsinkRows; }
+
+hipError_t launch_column_sum(const float* x, int rows, int cols, float scale, float* part,
+                             float* out, hipStream_t st) {
+  if (cols <= 0) return hipSuccess;
+  const int nslab = dsink_slabs(rows);
+  if (nslab > 0)
+    hipLaunchKernelGGL(column_sum_partial_kernel, dim3(nslab), dim3(256), 0, st, x, rows, cols, part);
+  hipLaunchKernelGGL(column_sum_final_kernel, dim3(cols), dim3(256), 0, st, part, nslab, cols, scale,
+                     out);
+  return hipGetLastError();
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, void* dst,
@@ -321,14 +335,7 @@ static void convert(const float* src, void* dst, size_t n, hipStream_t st) {
 
 hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq, void* dk,
                              void* dv, bool dq_from_acc, bool dkv_from_acc, hipStream_t st) {
-  if (dsink != nullptr) {
-    const int nslab = dsink_slabs(p.total);
-    if (nslab > 0)
-      hipLaunchKernelGGL(dsink_partial_kernel, dim3(nslab), dim3(256), 0, st, w.dsink_terms, p.total,
-                         p.hq, w.dsink_part);
-    hipLaunchKernelGGL(dsink_final_kernel, dim3(p.hq), dim3(256), 0, st, w.dsink_part, nslab, p.hq,
-                       dsink);
-  }
+  if (dsink != nullptr) launch_column_sum(w.dsink_terms, p.total, p.hq, 1.f, w.dsink_part, dsink, st);
   const size_t nq = static_cast<size_t>(p.total) * p.hq * p.d;
   const size_t nkv = static_cast<size_t>(p.total) * p.hkv * p.d;
   const bool f32 = p.dtype == SINK_ATTN_F32;

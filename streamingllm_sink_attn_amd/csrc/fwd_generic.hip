@@ -3,6 +3,9 @@
 // walked one at a time with an online softmax (running max m and sum l); the
 // sink enters only in the epilogue as the output scale
 // s = sigma(L_orig - a_h) ("Attention Sink, Learnable Sink and dsink", s4).
+// With gate0 != NULL it also writes the first-token gate (l - l_0) / l, the
+// share of the real-token softmax not on the sample's first key ("Paper
+// notes: Attention Sink and the native MoE in attention layers" s2, s5).
 #include "common.cuh"
 #include "row_keys.cuh"
 
@@ -12,7 +15,8 @@ template <typename T>
 __global__ __launch_bounds__(64) void fwd_generic_kernel(Prefill p, const void* __restrict__ q,
                                                          const void* __restrict__ k,
                                                          const void* __restrict__ v, void* o,
-                                                         float* lse, float* s_out) {
+                                                         float* lse, float* s_out,
+                                                         float* gate_out) {
   const int t = blockIdx.x;
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
@@ -32,6 +36,7 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(Prefill p, const void* 
     acc[r] = 0.f;
   }
   float m = -kInf, l = 0.f;
+  float l0 = 0.f;                        // probability mass of key 0 (same base as l)
 
   for_each_valid_key(p, b, i, g, [&](int j) {
     const size_t krow = (static_cast<size_t>(t0 + j) * p.hkv + g) * D;
@@ -48,6 +53,7 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(Prefill p, const void* 
     const float corr = __expf(m - m_new);
     const float pj = __expf(x - m_new);
     l = l * corr + pj;
+    l0 = j == 0 ? pj : l0 * corr;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int d = lane + 64 * r;
@@ -77,17 +83,19 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(Prefill p, const void* 
   if (lane == 0) {
     lse[static_cast<size_t>(t) * p.hq + h] = L_orig;
     if (s_out) s_out[static_cast<size_t>(t) * p.hq + h] = s_val;
+    if (gate_out) gate_out[static_cast<size_t>(t) * p.hq + h] = l > 0.f ? (l - l0) / l : 0.f;
   }
 }
 
 hipError_t launch_fwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
-                              void* o, float* lse, float* s, hipStream_t st) {
+                              void* o, float* lse, float* s, float* gate0, hipStream_t st) {
   if (p.total == 0) return hipSuccess;
   dim3 grid(p.total, p.hq);
   if (p.dtype == SINK_ATTN_F32)
-    hipLaunchKernelGGL(fwd_generic_kernel<float>, grid, dim3(64), 0, st, p, q, k, v, o, lse, s);
+    hipLaunchKernelGGL(fwd_generic_kernel<float>, grid, dim3(64), 0, st, p, q, k, v, o, lse, s, gate0);
   else
-    hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, grid, dim3(64), 0, st, p, q, k, v, o, lse, s);
+    hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, grid, dim3(64), 0, st, p, q, k, v, o, lse, s,
+                       gate0);
   return hipGetLastError();
 }
 

@@ -31,6 +31,13 @@
 //     and l always share the same base.
 //   * LDS addresses: the per-lane swizzled offsets are computed once; the
 //     loop is unrolled by two so buffer offsets are instruction immediates.
+//   * Optional first-token gate (instantiation GATE): the share of the
+//     real-token softmax that is not on the sample's first key, 1 - A_0, the
+//     vanilla-attention gate of "Paper notes: Attention Sink and the native
+//     MoE in attention layers" s2 (G = 1 - A_sink) and s5 (its LSE form).
+//     Key 0 of a sample is element (M-tile 0, i 0) of the lanes of half 0 in
+//     key tile 0, so its probability is kept beside the row sum (rescaled
+//     with it) and the epilogue writes (l - l_0) / l.
 #include <cstdlib>
 #include <type_traits>
 
@@ -64,13 +71,15 @@ __device__ __forceinline__ u32x2 lds_tr(const lds_char* base, int byte_off) {
                                        (__attribute__((address_space(3))) i16x4*)(base + byte_off)));
 }
 
+template <bool GATE>
 __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
                                                           const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           uint16_t* __restrict__ O,
                                                           float* __restrict__ lse_out,
-                                                          float* __restrict__ s_out) {
+                                                          float* __restrict__ s_out,
+                                                          float* __restrict__ gate_out) {
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][TILE];
   __shared__ uint32_t bitmap[BITMAP_LDS_WORDS];
@@ -145,6 +154,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
   float mrun = -kInf, lsum = 0.f;
+  float l0 = 0.f;                                    // GATE: P of the sample's first key
 
   const int kvs = p.hkv * D;
   const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
@@ -240,11 +250,13 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
         pend[cc] = __builtin_bit_cast(bf16x8, u);
       }
       lsum *= f;
+      if constexpr (GATE) l0 *= f;
       mrun = mnew;
     }
   };
-  // P = 2^(c x - mb) in bf16 as four k-steps, l += sum P.
-  auto probs = [&](f32x16 (&s)[2], float mb, bf16x8 (&pf)[4]) {
+  // P = 2^(c x - mb) in bf16 as four k-steps, l += sum P.  first: this is
+  // key tile 0 (GATE keeps the first key's P).
+  auto probs = [&](f32x16 (&s)[2], float mb, bool first, bf16x8 (&pf)[4]) {
     float ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -255,6 +267,9 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
         ls += e;
       }
     lsum += ls;
+    if constexpr (GATE) {
+      if (first) l0 += gq == 0 ? s[0][0] : 0.f;     // uniform branch
+    }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) pf[cc] = pack_kstep(s[cc >> 1], cc & 1);
   };
@@ -301,7 +316,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       f32x16 s0[2];
       scores(std::integral_constant<int, 0>{}, s0);
       const float mb = finish_scores(t_cur, s0, pf);
-      probs(s0, mb, pf);
+      probs(s0, mb, t_cur == 0, pf);
     }
     wait_bar<0>();
 
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       const float mb = finish_scores(t_nx, s_nx, pf);
       bf16x8 pn[4];
       pv(std::integral_constant<int, st>{}, pf);
-      probs(s_nx, mb, pn);
+      probs(s_nx, mb, t_nx == 0, pn);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) pf[cc] = pn[cc];
       // This step's loads landed and no read of the buffers they refill next
@@ -341,6 +356,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
 
   // Epilogue: L_orig = alpha*m + ln l; s = sigma(L_orig - a_h); O = acc * s / l.
   const float lt = xhalf_sum(lsum);
+  const float l0t = GATE ? xhalf_sum(l0) : 0.f;
   if (qi >= wq1) return;
   const bool has_sink = p.sink != nullptr;
   float L_orig, s_val, mul;
@@ -367,6 +383,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     const size_t r = static_cast<size_t>(t0 + qi) * p.hq + h;
     lse_out[r] = L_orig;
     if (s_out) s_out[r] = s_val;
+    if constexpr (GATE) gate_out[r] = lt > 0.f ? (lt - l0t) / lt : 0.f;
   }
 }
 
@@ -417,14 +434,15 @@ bool fwd_mfma_supported(const Prefill& p) {
 }
 
 hipError_t launch_fwd_mfma(const Prefill& p, const void* q, const void* k, const void* v, void* o,
-                           float* lse, float* s, hipStream_t st) {
+                           float* lse, float* s, float* gate0, hipStream_t st) {
   if (p.total == 0 || p.batch == 0) return hipSuccess;
   const qm::Geo geo = qm::make_geo(p, fwd128::FNW, fwd128::FQW);
   const long long grid = static_cast<long long>(geo.nptiles) * p.batch * geo.Z;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd128::fwd_kernel, dim3(static_cast<unsigned>(grid)), dim3(64 * fwd128::FNW), 0,
-                     st, p, geo, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, s);
+  auto kern = gate0 ? fwd128::fwd_kernel<true> : fwd128::fwd_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * fwd128::FNW), 0, st, p, geo,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, s, gate0);
   return hipGetLastError();
 }
 

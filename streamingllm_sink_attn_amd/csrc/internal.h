@@ -48,10 +48,11 @@ struct Decode {
 };
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----
+// gate0: float32 [T, Hq] first-token gate, or nullptr (not computed).
 hipError_t launch_fwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
-                              void* o, float* lse, float* s, hipStream_t st);
+                              void* o, float* lse, float* s, float* gate0, hipStream_t st);
 hipError_t launch_fwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
-                           void* o, float* lse, float* s, hipStream_t st);
+                           void* o, float* lse, float* s, float* gate0, hipStream_t st);
 bool fwd_mfma_supported(const Prefill& p);
 
 hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* lse,
@@ -68,6 +69,11 @@ int bwd_num_tiles(const Prefill& p);        // key tiles of the key-major pass
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st);
 int block_csr_words(const Prefill& p);      // 32-bit words per reverse-list bit row
 int dsink_slabs(int total);                 // row slabs of the dsink reduction
+// out[c] = scale * sum_r x[r, c] over the rows of x [rows, cols], in a fixed
+// order (per-slab partials in part [dsink_slabs(rows), cols], then slabs in
+// order): deterministic.
+hipError_t launch_column_sum(const float* x, int rows, int cols, float scale, float* part,
+                             float* out, hipStream_t st);
 hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq,
                              void* dk, void* dv, bool dq_from_acc, bool dkv_from_acc,
                              hipStream_t st);

@@ -290,20 +290,68 @@ int sink_attn_check_decode(const sink_attn_decode_desc* desc, const void* q, con
   return SINK_ATTN_OK;
 }
 
-int sink_attn_fwd(const sink_attn_prefill_desc* desc, const void* q, const void* k, const void* v,
-                  void* o, float* lse, float* s, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+int sink_attn_check_fwd_gated(const sink_attn_prefill_desc* desc, const void* q, const void* k,
+                              const void* v, const void* o, const float* lse, const float* s,
+                              const float* gate0, size_t workspace_bytes) {
+  SA_TRY(sink_attn_check_fwd(desc, q, k, v, o, lse, s, workspace_bytes));
+  SA_TRY(check_ptr(gate0, "gate0", 4, false));
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_fwd_gated(const sink_attn_prefill_desc* desc, const void* q, const void* k,
+                        const void* v, void* o, float* lse, float* s, float* gate0,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    SA_TRY(sink_attn_check_fwd(desc, q, k, v, o, lse, s, workspace_bytes));
+    SA_TRY(sink_attn_check_fwd_gated(desc, q, k, v, o, lse, s, gate0, workspace_bytes));
     (void)workspace;
     const sa::Prefill p = to_prefill(desc);
     if (p.total == 0) return SINK_ATTN_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = sa::fwd_mfma_supported(p) ? sa::launch_fwd_mfma(p, q, k, v, o, lse, s, st)
-                                             : sa::launch_fwd_generic(p, q, k, v, o, lse, s, st);
+    hipError_t e = sa::fwd_mfma_supported(p)
+                       ? sa::launch_fwd_mfma(p, q, k, v, o, lse, s, gate0, st)
+                       : sa::launch_fwd_generic(p, q, k, v, o, lse, s, gate0, st);
     return hip_status(e, "sink_attn_fwd launch");
   } catch (...) {
     return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_fwd");
+  }
+}
+
+int sink_attn_fwd(const sink_attn_prefill_desc* desc, const void* q, const void* k, const void* v,
+                  void* o, float* lse, float* s, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return sink_attn_fwd_gated(desc, q, k, v, o, lse, s, nullptr, workspace, workspace_bytes, stream);
+}
+
+size_t sink_attn_head_importance_workspace_size(int32_t rows, int32_t num_heads) {
+  if (rows <= 0 || num_heads <= 0) return 0;
+  return round_up(static_cast<size_t>(sa::dsink_slabs(rows)) * num_heads * 4);
+}
+
+int sink_attn_check_head_importance(const float* gate, int32_t rows, int32_t num_heads,
+                                    const float* imp, size_t workspace_bytes) {
+  if (rows < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "rows < 0");
+  if (num_heads < 1) return fail(SINK_ATTN_INVALID_ARGUMENT, "num_heads < 1");
+  SA_TRY(check_ptr(gate, "gate", 4, rows > 0));
+  SA_TRY(check_ptr(imp, "imp", 4, true));
+  const size_t need = sink_attn_head_importance_workspace_size(rows, num_heads);
+  if (workspace_bytes < need)
+    return fail(SINK_ATTN_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu", workspace_bytes, need);
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_head_importance(const float* gate, int32_t rows, int32_t num_heads, float* imp,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    SA_TRY(sink_attn_check_head_importance(gate, rows, num_heads, imp, workspace_bytes));
+    if (sink_attn_head_importance_workspace_size(rows, num_heads) > 0 && workspace == nullptr)
+      return fail(SINK_ATTN_INVALID_ARGUMENT, "workspace is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const float scale = rows > 0 ? 1.f / static_cast<float>(rows) : 0.f;
+    hipError_t e = sa::launch_column_sum(gate, rows, num_heads, scale, static_cast<float*>(workspace),
+                                         imp, st);
+    return hip_status(e, "sink_attn_head_importance launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_head_importance");
   }
 }
 

@@ -145,3 +145,32 @@ def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libsinkattn.so")
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_check_fwd_gated_and_head_importance():
+    L = B.lib()
+
+    def chk_g(desc, gate0=FAKE, **kw):
+        p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, s=FAKE)
+        p.update(kw)
+        return L.sink_attn_check_fwd_gated(ctypes.byref(desc), p["q"], p["k"], p["v"], p["o"],
+                                           p["lse"], p["s"], gate0, 0)
+    assert chk_g(_desc()) == B.OK
+    assert chk_g(_desc(), gate0=None) == B.OK                       # gate optional
+    assert chk_g(_desc(), gate0=FAKE + 2) == B.INVALID_ARGUMENT     # misaligned
+    assert chk_g(_desc(head_dim=100)) == B.UNSUPPORTED              # the forward's own checks
+
+    def chk_i(rows, heads, gate=FAKE, imp=FAKE, ws=None):
+        if ws is None:
+            ws = L.sink_attn_head_importance_workspace_size(rows, heads)
+        return L.sink_attn_check_head_importance(gate, rows, heads, imp, ws)
+    assert chk_i(1000, 32) == B.OK
+    need = L.sink_attn_head_importance_workspace_size(1000, 32)
+    assert need >= 32 * 4 * (1000 // 64)
+    assert chk_i(1000, 32, ws=need - 1) == B.WORKSPACE_TOO_SMALL
+    assert chk_i(0, 32, gate=None) == B.OK                           # no rows: gate not needed
+    assert L.sink_attn_head_importance_workspace_size(0, 32) == 0
+    assert chk_i(-1, 32) == B.INVALID_ARGUMENT
+    assert chk_i(10, 0) == B.INVALID_ARGUMENT
+    assert chk_i(10, 4, imp=None) == B.INVALID_ARGUMENT
+    assert chk_i(10, 4, gate=FAKE + 1) == B.INVALID_ARGUMENT
