@@ -255,6 +255,45 @@ def bench_decode(torch, sa, W, steps, warmup):
                        "head_dim": wl.d}}
 
 
+def bench_kvcache_q8_decode(torch, sa, W, steps, warmup):
+    """Decode over the 8-bit rolling cache: 128 sequences x (4 first tokens in
+    bf16 + a 4092-token e4m3 ring), Hq=64, Hkv=8 (the bf16 decode's shape).
+    Two cache copies alternate; bytes count each valid slot once (bf16 first
+    tokens, 8-bit ring rows and their two scales) plus Q, O, lse, s."""
+    wl = W.kvcache_q8_decode()
+    caches = []
+    for i in range(2):
+        c = sa.KvCache(wl.batch, wl.n_sink, wl.window, wl.hkv, wl.d, quantized=True)
+        c.sink_k.copy_(torch.from_numpy(wl.sink_k).to(torch.bfloat16))
+        c.sink_v.copy_(torch.from_numpy(wl.sink_v).to(torch.bfloat16))
+        c.win_k.copy_(torch.roll(torch.from_numpy(wl.win_k), i, dims=1))
+        c.win_v.copy_(torch.roll(torch.from_numpy(wl.win_v), i, dims=1))
+        c.win_k_scale.copy_(torch.from_numpy(wl.win_k_scale))
+        c.win_v_scale.copy_(torch.from_numpy(wl.win_v_scale))
+        caches.append(c)
+    q = torch.from_numpy(wl.q).cuda().to(torch.bfloat16)
+    nt = torch.from_numpy(wl.n_tokens).cuda()
+    sink = torch.from_numpy(wl.sink).cuda()
+    o = torch.empty_like(q)
+    B, H, D = wl.batch, wl.hkv, wl.d
+    nbytes = (2 * B * wl.n_sink * H * D * 2 + 2 * B * wl.window * H * D + 2 * B * H * wl.window * 4
+              + 2 * B * wl.hq * D * 2 + 2 * B * wl.hq * 4)
+    it = [0]
+
+    def step():
+        i = it[0] & 1
+        it[0] += 1
+        sa.kvcache_decode(caches[i], q, nt, wl.scale, sink, out=o)
+
+    ms, _ = Timer(torch).run(step, steps, warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "streaming_decode_q8", "unit": "GB/s", "value": round(gbs, 1),
+            "ms_per_step": round(ms, 4), "bytes_per_step": nbytes,
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "config": {"batch": B, "n_sink": wl.n_sink, "window": wl.window, "hq": wl.hq,
+                       "hkv": H, "head_dim": D, "ring": "e4m3 + per-row float32 scales"}}
+
+
 def cpu_baseline(W, budget_s=15.0):
     """The float64 oracle on whole (sample, head) units of the same workload,
     until about budget_s seconds of CPU work; reported in TFLOP/s counted the
@@ -296,7 +335,8 @@ def main():
                     help="untimed steps first: the GPU reaches its steady clocks only after "
                          "tens of milliseconds of load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks", "gated"),
+    ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks", "gated",
+                                       "decode_q8"),
                     default="all",
                     help="headline: only the GQA prefill forward (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -321,7 +361,8 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     single = {"decode": bench_decode, "streaming": bench_streaming_prefill,
-              "blocks": bench_block_sparse, "gated": bench_gqa_gated}
+              "blocks": bench_block_sparse, "gated": bench_gqa_gated,
+              "decode_q8": bench_kvcache_q8_decode}
     if args.legs in single:
         print(json.dumps(single[args.legs](torch, sa, W, args.steps, args.warmup)), flush=True)
         return
@@ -348,8 +389,8 @@ def main():
         "roofline": roofline,
     }
     also = []
-    legs = ((bench_streaming_prefill, bench_decode, bench_block_sparse, bench_gqa_gated)
-            if args.legs == "all" else ())
+    legs = ((bench_streaming_prefill, bench_decode, bench_block_sparse, bench_gqa_gated,
+             bench_kvcache_q8_decode) if args.legs == "all" else ())
     for fn in legs:
         try:
             also.append(fn(torch, sa, W, args.steps, args.warmup))

@@ -155,6 +155,80 @@ typedef struct sink_attn_decode_desc {
 } sink_attn_decode_desc;
 
 /*
+ * StreamingLLM's rolling KV cache ("What is Attention Sink? ... StreamingLLM"
+ * (model.playoffer.cn), core idea: the first tokens of the stream (4
+ * recommended) stay for good, a sliding window keeps the most recent ones and
+ * a new token replaces the oldest window token; "Attention Sink"
+ * (lijianxiong.space), H2O section: the recent part as a circular queue).
+ * The token at stream position p lives in sink slot p when p < n_sink, else
+ * in ring slot (p - n_sink) mod window.
+ *
+ * quantized = 0: one bfloat16 cache per K and V, [B, n_sink + window, Hkv, D]
+ *   (slots [0, n_sink) the first tokens, n_sink + r ring slot r): the layout
+ *   sink_attn_decode reads.
+ * quantized = 1 (head_dim 128): the first tokens stay bfloat16 and the ring
+ *   is 8-bit, as the same page's engineering notes describe for KV-cache
+ *   quantisers that keep the first tokens in high precision:
+ *     sink_k, sink_v            bfloat16 [B, n_sink, Hkv, D];
+ *     win_k, win_v              e4m3 codes [B, window, Hkv, D] (OCP layout: 1
+ *                               sign, 4 exponent bits of bias 7, 3 mantissa
+ *                               bits; 448 the largest value);
+ *     win_k_scale, win_v_scale  float32 [B, Hkv, window]; a ring row's value
+ *                               is code * scale, with scale = amax / 448 and
+ *                               code = e4m3(x * (448 / amax)) rounded to
+ *                               nearest even (a zero row: scale 0, codes 0).
+ * All pointers are device memory owned by the caller; unused ones may be NULL.
+ */
+typedef struct sink_attn_kvcache_desc {
+  int32_t batch;
+  int32_t n_sink;         /* first tokens kept for good (>= 0) */
+  int32_t window;         /* most recent tokens kept in the ring (>= 1) */
+  int32_t num_kv_heads;
+  int32_t head_dim;       /* multiple of 8 up to SINK_ATTN_MAX_HEAD_DIM; 128 when quantized */
+  int32_t quantized;      /* 0 or 1, see above */
+  void* k;                /* quantized = 0 */
+  void* v;
+  void* sink_k;           /* quantized = 1 */
+  void* sink_v;
+  void* win_k;
+  void* win_v;
+  float* win_k_scale;
+  float* win_v_scale;
+} sink_attn_kvcache_desc;
+
+/*
+ * Append a chunk of new tokens to every sequence's cache.
+ *   k_new, v_new  bfloat16 [B, chunk, Hkv, D]: the new tokens in stream order.
+ *   n_seen        device int32 [B]: tokens each stream held before this call;
+ *                 token c of sequence b has stream position n_seen[b] + c.
+ * Each token is written to its slot (quantized ring rows with their scales),
+ * overwriting the token that slot held; a chunk token that a later token of
+ * the same chunk would overwrite at once is not written, so no slot has two
+ * writers.  The caller advances n_seen by chunk for the next call.
+ */
+int sink_attn_kvcache_append(const sink_attn_kvcache_desc* cache, const void* k_new,
+                             const void* v_new, int32_t chunk, const int32_t* n_seen,
+                             void* stream);
+
+/*
+ * Decode one query per sequence over its cache: [Notes] s1 and s4 on the
+ * slots written so far, split-KV merged by log-sum-exp (as sink_attn_decode).
+ *   q         bfloat16 [B, num_q_heads, D].
+ *   n_tokens  device int32 [B]: tokens appended to each stream so far, the
+ *             current token included; the valid slots are the first
+ *             min(n_tokens, n_sink) sink slots and the first
+ *             min(max(n_tokens - n_sink, 0), window) ring slots.
+ *   o         output bfloat16 [B, num_q_heads, D]; lse, s float32 [B, num_q_heads]
+ *             as sink_attn_decode (s may be NULL).
+ *   workspace sink_attn_kvcache_decode_workspace_size bytes.
+ */
+int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
+                             int32_t num_q_heads, const int32_t* n_tokens, float softmax_scale,
+                             const float* learnable_sink, int32_t num_splits,
+                             void* o, float* lse, float* s,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward.  [Notes] s1 (scores, probabilities, output) and s4 (the sink as an
  * output scale).
  *   q, k, v   inputs (layouts above).
@@ -239,6 +313,8 @@ size_t sink_attn_fwd_workspace_size(const sink_attn_prefill_desc* desc);
 size_t sink_attn_bwd_workspace_size(const sink_attn_prefill_desc* desc);
 size_t sink_attn_decode_workspace_size(const sink_attn_decode_desc* desc);
 size_t sink_attn_head_importance_workspace_size(int32_t rows, int32_t num_heads);
+size_t sink_attn_kvcache_decode_workspace_size(const sink_attn_kvcache_desc* cache,
+                                               int32_t num_q_heads, int32_t num_splits);
 
 /*
  * Pure host validation of the scalar arguments and pointers of the matching
@@ -264,6 +340,12 @@ int sink_attn_check_fwd_gated(const sink_attn_prefill_desc* desc,
                               const float* gate0, size_t workspace_bytes);
 int sink_attn_check_head_importance(const float* gate, int32_t rows, int32_t num_heads,
                                     const float* imp, size_t workspace_bytes);
+int sink_attn_check_kvcache_append(const sink_attn_kvcache_desc* cache, const void* k_new,
+                                   const void* v_new, int32_t chunk, const int32_t* n_seen);
+int sink_attn_check_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
+                                   int32_t num_q_heads, const int32_t* n_tokens,
+                                   float softmax_scale, int32_t num_splits, const void* o,
+                                   const float* lse, const float* s, size_t workspace_bytes);
 
 /* Static description of a status code; never NULL. */
 const char* sink_attn_strerror(int status);

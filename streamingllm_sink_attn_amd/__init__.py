@@ -4,8 +4,9 @@ The compute lives in ``libsinkattn.so`` (HIP kernels behind a C ABI declared
 in ``include/sink_attn.h``); :mod:`.binding` marshals torch tensors into it.
 :mod:`.workloads` draws the seeded synthetic inputs.
 """
-from .binding import (SinkAttnError, bwd, debug_visit_map, decode, fwd, fwd_gated,  # noqa: F401
-                      head_importance, lib, prefill_path)
+from .binding import (KvCache, SinkAttnError, bwd, debug_visit_map, decode, fwd,  # noqa: F401
+                      fwd_gated, head_importance, kvcache_append, kvcache_decode, lib,
+                      prefill_path)
 
-__all__ = ["fwd", "fwd_gated", "head_importance", "bwd", "decode", "debug_visit_map", "prefill_path",
-           "lib", "SinkAttnError"]
+__all__ = ["fwd", "fwd_gated", "head_importance", "bwd", "decode", "KvCache", "kvcache_append",
+           "kvcache_decode", "debug_visit_map", "prefill_path", "lib", "SinkAttnError"]

@@ -45,6 +45,25 @@ class PrefillDesc(ctypes.Structure):
     ]
 
 
+class KvCacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_i32),
+        ("n_sink", c_i32),
+        ("window", c_i32),
+        ("num_kv_heads", c_i32),
+        ("head_dim", c_i32),
+        ("quantized", c_i32),
+        ("k", c_vp),
+        ("v", c_vp),
+        ("sink_k", c_vp),
+        ("sink_v", c_vp),
+        ("win_k", c_vp),
+        ("win_v", c_vp),
+        ("win_k_scale", c_vp),
+        ("win_v_scale", c_vp),
+    ]
+
+
 class DecodeDesc(ctypes.Structure):
     _fields_ = [
         ("cache_seqlens", c_vp),
@@ -77,6 +96,13 @@ _SIGS = {
     "sink_attn_check_fwd_gated": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           ctypes.c_size_t]),
     "sink_attn_check_head_importance": (c_i32, [c_vp, c_i32, c_i32, c_vp, ctypes.c_size_t]),
+    "sink_attn_kvcache_append": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    "sink_attn_kvcache_decode": (c_i32, [c_vp, c_vp, c_i32, c_vp, ctypes.c_float, c_vp, c_i32, c_vp,
+                                         c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_kvcache_decode_workspace_size": (ctypes.c_size_t, [c_vp, c_i32, c_i32]),
+    "sink_attn_check_kvcache_append": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
+    "sink_attn_check_kvcache_decode": (c_i32, [c_vp, c_vp, c_i32, c_vp, ctypes.c_float, c_i32, c_vp,
+                                               c_vp, c_vp, ctypes.c_size_t]),
     "sink_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               c_vp, ctypes.c_size_t, c_vp]),
     "sink_attn_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
@@ -273,6 +299,75 @@ def decode(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, learnabl
     ws = _workspace(ws_bytes, q.device)
     _check(L.sink_attn_decode(ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(o), _p(lse),
                               _p(s), _p(ws), ws_bytes, _stream(stream)))
+    return o, lse, s
+
+
+class KvCache:
+    """StreamingLLM rolling KV cache in device memory (the layouts of
+    sink_attn_kvcache_desc): bfloat16 [B, n_sink + window, Hkv, D] K and V, or
+    with ``quantized`` bfloat16 first tokens plus an e4m3 ring with float32
+    scales."""
+
+    def __init__(self, batch, n_sink, window, num_kv_heads, head_dim=128, quantized=False,
+                 device="cuda"):
+        self.batch, self.n_sink, self.window = int(batch), int(n_sink), int(window)
+        self.hkv, self.d, self.quantized = int(num_kv_heads), int(head_dim), bool(quantized)
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        B, hkv, d = self.batch, self.hkv, self.d
+        if not self.quantized:
+            self.k = z((B, n_sink + window, hkv, d), torch.bfloat16)
+            self.v = z((B, n_sink + window, hkv, d), torch.bfloat16)
+            self.sink_k = self.sink_v = self.win_k = self.win_v = None
+            self.win_k_scale = self.win_v_scale = None
+        else:
+            self.k = self.v = None
+            self.sink_k = z((B, n_sink, hkv, d), torch.bfloat16)
+            self.sink_v = z((B, n_sink, hkv, d), torch.bfloat16)
+            self.win_k = z((B, window, hkv, d), torch.uint8)
+            self.win_v = z((B, window, hkv, d), torch.uint8)
+            self.win_k_scale = z((B, hkv, window), torch.float32)
+            self.win_v_scale = z((B, hkv, window), torch.float32)
+
+    def desc(self) -> KvCacheDesc:
+        ptr = lambda t: t.data_ptr() if t is not None and t.numel() > 0 else None
+        return KvCacheDesc(batch=self.batch, n_sink=self.n_sink, window=self.window,
+                           num_kv_heads=self.hkv, head_dim=self.d, quantized=int(self.quantized),
+                           k=ptr(self.k), v=ptr(self.v), sink_k=ptr(self.sink_k),
+                           sink_v=ptr(self.sink_v), win_k=ptr(self.win_k), win_v=ptr(self.win_v),
+                           win_k_scale=ptr(self.win_k_scale), win_v_scale=ptr(self.win_v_scale))
+
+
+def kvcache_append(cache: KvCache, k_new, v_new, n_seen, stream=None):
+    """Append k_new, v_new (bf16 [B, C, Hkv, D]) at stream positions n_seen[b] + c."""
+    _need_cuda(k_new, v_new, n_seen)
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise SinkAttnError(UNSUPPORTED, "the cache takes bfloat16 tokens")
+    if n_seen.dtype != torch.int32:
+        raise SinkAttnError(INVALID_ARGUMENT, "n_seen must be int32")
+    desc = cache.desc()
+    _check(lib().sink_attn_kvcache_append(ctypes.byref(desc), _p(k_new), _p(v_new),
+                                          int(k_new.shape[1]), _p(n_seen), _stream(stream)))
+
+
+def kvcache_decode(cache: KvCache, q, n_tokens, softmax_scale=None, learnable_sink=None,
+                   num_splits=0, return_s=True, out=None, stream=None):
+    """Decode one query per sequence over the cache (n_tokens[b] tokens appended,
+    the current one included).  Returns (o, lse, s or None)."""
+    _need_cuda(q, n_tokens, learnable_sink)
+    if n_tokens.dtype != torch.int32:
+        raise SinkAttnError(INVALID_ARGUMENT, "n_tokens must be int32")
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    B, hq, _ = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
+    desc = cache.desc()
+    L = lib()
+    ws_bytes = L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(desc), hq, int(num_splits))
+    ws = _workspace(ws_bytes, q.device)
+    _check(L.sink_attn_kvcache_decode(ctypes.byref(desc), _p(q), hq, _p(n_tokens), float(scale),
+                                      _p(learnable_sink), int(num_splits), _p(o), _p(lse), _p(s),
+                                      _p(ws), ws_bytes, _stream(stream)))
     return o, lse, s
 
 

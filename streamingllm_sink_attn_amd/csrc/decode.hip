@@ -26,6 +26,15 @@
 //     split, applies the sink epilogue itself and writes O, LSE and s.
 // Merge kernel (more than one split): M = max_k m_k, l = sum_k e^{m_k - M}
 // l_k, L_orig = M + ln l, O = s * sum_k e^{m_k - M} acc_k / l.
+//
+// 8-bit cache (instantiation Q8): the first n_sink tokens are bfloat16 rows
+// of one array and the ring of recent tokens e4m3 rows of another, with a
+// float32 scale per (slot, KV head).  Slots are numbered sinks first (padded
+// to a whole 32-slot chunk) then ring slots, so every chunk is all-bf16 or
+// all-e4m3 and the choice is uniform per wavefront.  e4m3 codes convert to
+// bfloat16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1); the K scale of
+// a slot multiplies its scores, the V scale its probability in P V (not in
+// the row sum l), so no row is rescaled element by element.
 #include "common.cuh"
 
 namespace sa {
@@ -65,6 +74,17 @@ __device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_ptr) {
       (__attribute__((address_space(3))) i16x4*)(const_cast<uint16_t*>(lds_ptr)));
 }
 
+// Two e4m3 codes (the 16-bit half `hi` of w) as two bfloat16, exactly.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+}
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{fp8x2_to_bf16x2(w0, false), fp8x2_to_bf16x2(w0, true), fp8x2_to_bf16x2(w1, false),
+               fp8x2_to_bf16x2(w1, true)};
+}
+
+template <bool Q8>
 __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
                                                        const uint16_t* __restrict__ Q,
                                                        const uint16_t* __restrict__ KC,
@@ -72,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
                                                        float* __restrict__ ws,
                                                        uint16_t* __restrict__ O,
                                                        float* __restrict__ lse,
-                                                       float* __restrict__ s_out) {
+                                                       float* __restrict__ s_out, KvCache qc) {
   // Per-wavefront double-buffered V chunks; after the loop the same memory
   // holds the wavefronts' partial results for the merge.
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][2][VBUF];
@@ -87,8 +107,20 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
   const int G = p.hq / p.hkv;
   const int h0 = g * G + hg * HN;                    // first query head of the group
   const int nh = min(HN, G - hg * HN);               // heads in this workgroup
-  const int n = p.cache_seqlens ? min(p.cache_seqlens[b], p.slots) : p.slots;
-  const int per = (p.slots + p.splits - 1) / p.splits;
+  int n, per;
+  int ns = 0, ns_pad = 0;                            // Q8: valid sinks, sink chunks' slots
+  if constexpr (!Q8) {
+    n = p.cache_seqlens ? min(p.cache_seqlens[b], p.slots) : p.slots;
+    per = (p.slots + p.splits - 1) / p.splits;
+  } else {
+    const int tokens = p.cache_seqlens[b];           // appended so far, the current one included
+    ns = min(tokens, qc.n_sink);
+    const int nw = min(max(tokens - qc.n_sink, 0), qc.window);
+    ns_pad = (ns + CH - 1) / CH * CH;
+    n = ns_pad + nw;
+    const int span = (qc.n_sink + CH - 1) / CH * CH + qc.window;   // the same for every sequence
+    per = ((span + CH - 1) / CH + p.splits - 1) / p.splits * CH;   // whole chunks per split
+  }
   const int s0 = split * per;
   const int s1 = min(n, s0 + per);
 
@@ -110,8 +142,14 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
   }
 
   const size_t row_stride = static_cast<size_t>(p.hkv) * D;
-  const uint16_t* Kb = KC + (static_cast<size_t>(b) * p.slots * p.hkv + g) * D;
-  const uint16_t* Vb = VC + (static_cast<size_t>(b) * p.slots * p.hkv + g) * D;
+  const int kv_slots = Q8 ? qc.n_sink : p.slots;     // rows per sequence of KC / VC
+  const uint16_t* Kb = KC + (static_cast<size_t>(b) * kv_slots * p.hkv + g) * D;
+  const uint16_t* Vb = VC + (static_cast<size_t>(b) * kv_slots * p.hkv + g) * D;
+  // Q8 ring rows (bytes) and scales of this (sequence, KV head).
+  const uint8_t* Kw = Q8 ? qc.win_k + (static_cast<size_t>(b) * qc.window * p.hkv + g) * D : nullptr;
+  const uint8_t* Vw = Q8 ? qc.win_v + (static_cast<size_t>(b) * qc.window * p.hkv + g) * D : nullptr;
+  const float* Ksc = Q8 ? qc.win_k_scale + (static_cast<size_t>(b) * p.hkv + g) * qc.window : nullptr;
+  const float* Vsc = Q8 ? qc.win_v_scale + (static_cast<size_t>(b) * p.hkv + g) * qc.window : nullptr;
   const float c = p.scale * kLog2e;
   const float thr = kRescaleLog2 / c;
 
@@ -125,31 +163,77 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
   const int my_first = w;
   u32x4 kf[2][4], kn[2][4];     // current / next chunk K fragments [mt][ks]
   u32x4 vr[8];                  // next chunk V rows, 8 x 16 B per lane
+  // Q8: whether the current / next chunk is ring (e4m3: K and V hold the raw
+  // codes in words 0-1 until converted) and its slots' K / V scales.
+  bool cur_win = false, nxt_win = false;
+  float ksc[8], vsc[8], ksn[8], vsn[8];
+  const int ring_last = Q8 ? max(qc.window - 1, 0) : 0;
+  const int sink_last = Q8 ? max(ns - 1, 0) : 0;
 
   auto load_k = [&](int cs, u32x4 (&dst)[2][4]) {
+    if constexpr (Q8) {
+      if (cs >= ns_pad) {                            // uniform: a ring chunk
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int r = min(cs - ns_pad + mt * 16 + l16, ring_last);
+          const uint8_t* src = Kw + static_cast<size_t>(r) * row_stride + gq * 8;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(src + ks * 32);
+            dst[mt][ks] = u32x4{w[0], w[1], 0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = min(cs - ns_pad + 16 * mt + 4 * gq + i, ring_last);
+            ksn[mt * 4 + i] = Ksc[r];
+            vsn[mt * 4 + i] = Vsc[r];
+          }
+        return;
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       int slot = cs + mt * 16 + l16;
-      slot = slot < p.slots ? slot : p.slots - 1;
+      if constexpr (Q8) slot = min(slot, sink_last);
+      else slot = slot < p.slots ? slot : p.slots - 1;
       const uint16_t* src = Kb + static_cast<size_t>(slot) * row_stride + gq * 8;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
     }
   };
   auto load_v = [&](int cs) {
+    if constexpr (Q8) {
+      if (cs >= ns_pad) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = min(cs - ns_pad + (lane >> 4) + 4 * i, ring_last);
+          const u32x2 w = *reinterpret_cast<const u32x2*>(Vw + static_cast<size_t>(r) * row_stride + l16 * 8);
+          vr[i] = u32x4{w[0], w[1], 0u, 0u};
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int slot = cs + (lane >> 4) + 4 * i;
-      slot = slot < p.slots ? slot : p.slots - 1;
+      if constexpr (Q8) slot = min(slot, sink_last);
+      else slot = slot < p.slots ? slot : p.slots - 1;
       vr[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(slot) * row_stride + l16 * 8);
     }
   };
-  auto store_v = [&](uint16_t* buf) {
+  auto store_v = [&](uint16_t* buf, bool win) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = (lane >> 4) + 4 * i;
       const int pc = l16 ^ vswz(row);
-      *reinterpret_cast<u32x4*>(buf + row * D + pc * 8) = vr[i];
+      u32x4 x = vr[i];
+      if constexpr (Q8) {
+        if (win) x = fp8x8_to_bf16x8(x[0], x[1]);
+      }
+      *reinterpret_cast<u32x4*>(buf + row * D + pc * 8) = x;
     }
   };
 
@@ -159,7 +243,12 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
     const int cs = s0 + CH * ci;
     load_k(cs, kf);
     load_v(cs);
-    store_v(vbuf[w][0]);
+    if constexpr (Q8) {
+      cur_win = cs >= ns_pad;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { ksc[e] = ksn[e]; vsc[e] = vsn[e]; }
+    }
+    store_v(vbuf[w][0], cur_win);
   }
   while (ci < nchunks_total) {
     const int cs = s0 + CH * ci;
@@ -168,6 +257,15 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
     if (has_next) {
       load_k(s0 + CH * cn, kn);
       load_v(s0 + CH * cn);
+      if constexpr (Q8) nxt_win = s0 + CH * cn >= ns_pad;
+    }
+    if constexpr (Q8) {
+      if (cur_win) {                                 // e4m3 codes -> bf16, exactly
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = fp8x8_to_bf16x8(kf[mt][ks][0], kf[mt][ks][1]);
+      }
     }
     // S^T = K Q^T for 32 slots (2 M-tiles of 16) x 16 heads.
     f32x4 sacc[2];
@@ -178,14 +276,24 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
       for (int ks = 0; ks < 4; ++ks)
         sacc[mt] = mfma16(__builtin_bit_cast(bf16x8, kf[mt][ks]), qf[ks], sacc[mt]);
     }
+    if constexpr (Q8) {
+      if (cur_win) {                                 // the slots' K scales
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[mt][i] *= ksc[mt * 4 + i];
+      }
+    }
     // Mask slots past the split or the valid length.  Element i of lane
-    // (l16, gq) in M-tile mt is slot cs + 16mt + 4gq + i, head l16.
-    if (cs + CH > s1) {
+    // (l16, gq) in M-tile mt is slot cs + 16mt + 4gq + i, head l16.  Q8: a
+    // sink chunk's slots past the valid sinks too.
+    const int lim = (Q8 && cs < ns_pad) ? min(s1, ns) : s1;
+    if (cs + CH > lim) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (cs + 16 * mt + 4 * gq + i >= s1) sacc[mt][i] = -kInf;
+          if (cs + 16 * mt + 4 * gq + i >= lim) sacc[mt][i] = -kInf;
     }
     float mx = -kInf;
 #pragma unroll
@@ -214,6 +322,12 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
         pv[mt * 4 + i] = e;
         lpart += e;
       }
+    if constexpr (Q8) {
+      if (cur_win) {                                 // the slots' V scales, in P V only
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] *= vsc[e];
+      }
+    }
     // B operand: logical k slot t of quarter gq = slot 16*(t/4) + 4gq + t%4.
     const bf16x8 pf = __builtin_bit_cast(
         bf16x8, u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -235,11 +349,16 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
       oacc[dt] = mfma16(af, pf, oacc[dt]);
     }
     if (has_next) {
-      store_v(vbuf[w][cur ^ 1]);
+      store_v(vbuf[w][cur ^ 1], nxt_win);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kf[mt][ks] = kn[mt][ks];
+      if constexpr (Q8) {
+        cur_win = nxt_win;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { ksc[e] = ksn[e]; vsc[e] = vsn[e]; }
+      }
     }
     cur ^= 1;
     ci = cn;
@@ -386,9 +505,30 @@ hipError_t launch_decode(const Decode& p, const void* q, const void* kc, const v
   const int G = p.hq / p.hkv;
   const int nhg = (G + dec128::HN - 1) / dec128::HN;
   dim3 grid(p.splits, p.hkv * nhg, p.batch);
-  hipLaunchKernelGGL(dec128::split_kernel, grid, dim3(256), 0, st, p, nhg,
+  hipLaunchKernelGGL(dec128::split_kernel<false>, grid, dim3(256), 0, st, p, nhg,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), ws, static_cast<uint16_t*>(o), lse, s);
+                     static_cast<const uint16_t*>(vc), ws, static_cast<uint16_t*>(o), lse, s,
+                     KvCache{});
+  if (p.splits > 1)
+    hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3(p.batch * p.hq), dim3(128), 0, st, p, ws,
+                       o, lse, s);
+  return hipGetLastError();
+}
+
+int kvcache_q8_auto_splits(const Decode& p, const KvCache& c) {
+  Decode d = p;
+  d.slots = (c.n_sink + dec128::CH - 1) / dec128::CH * dec128::CH + c.window;
+  return decode_auto_splits(d);
+}
+
+hipError_t launch_kvcache_decode_q8(const Decode& p, const KvCache& c, const void* q, void* o,
+                                    float* lse, float* s, float* ws, hipStream_t st) {
+  const int G = p.hq / p.hkv;
+  const int nhg = (G + dec128::HN - 1) / dec128::HN;
+  dim3 grid(p.splits, p.hkv * nhg, p.batch);
+  hipLaunchKernelGGL(dec128::split_kernel<true>, grid, dim3(256), 0, st, p, nhg,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c.sink_k),
+                     static_cast<const uint16_t*>(c.sink_v), ws, static_cast<uint16_t*>(o), lse, s, c);
   if (p.splits > 1)
     hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3(p.batch * p.hq), dim3(128), 0, st, p, ws,
                        o, lse, s);

@@ -47,6 +47,21 @@ struct Decode {
   int splits;
 };
 
+// Rolling KV cache of StreamingLLM: n_sink first tokens plus a ring of the
+// last `window` tokens; quantized = the ring in 8-bit e4m3 with per-(slot,
+// KV head) float32 scales, the first tokens bfloat16.
+struct KvCache {
+  int batch, n_sink, window, hkv, d, quantized;
+  void* k;                    // !quantized: bf16 [B, n_sink + window, Hkv, D]
+  void* v;
+  void* sink_k;               // quantized: bf16 [B, n_sink, Hkv, D]
+  void* sink_v;
+  uint8_t* win_k;             // quantized: e4m3 [B, window, Hkv, D]
+  uint8_t* win_v;
+  float* win_k_scale;         // quantized: [B, Hkv, window]
+  float* win_v_scale;
+};
+
 // ---- launchers (each returns hipGetLastError() of its launches) ----
 // gate0: float32 [T, Hq] first-token gate, or nullptr (not computed).
 hipError_t launch_fwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
@@ -84,6 +99,16 @@ int decode_auto_splits(const Decode& p);
 bool decode_mfma_supported(const Decode& p);
 
 hipError_t launch_visit_map(const Prefill& p, uint8_t* out, hipStream_t st);
+
+// Append `chunk` tokens per sequence (k_new, v_new bf16 [B, chunk, Hkv, D],
+// stream positions n_seen[b] + c) into the cache.
+hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void* v_new, int chunk,
+                                 const int32_t* n_seen, hipStream_t st);
+// Decode over the 8-bit cache: p.cache_seqlens holds the tokens appended so
+// far per sequence (the current one included); p.slots is unused.
+hipError_t launch_kvcache_decode_q8(const Decode& p, const KvCache& c, const void* q, void* o,
+                                    float* lse, float* s, float* ws, hipStream_t st);
+int kvcache_q8_auto_splits(const Decode& p, const KvCache& c);
 
 // Fill kernels (used instead of hipMemsetAsync so callers may capture graphs).
 hipError_t launch_fill_zero(float* ptr, size_t n, hipStream_t st);

@@ -188,6 +188,77 @@ int hip_status(hipError_t e, const char* what) {
   return SINK_ATTN_OK;
 }
 
+int check_kvcache_desc(const sink_attn_kvcache_desc* c) {
+  if (c == nullptr) return fail(SINK_ATTN_INVALID_ARGUMENT, "cache desc is NULL");
+  if (c->batch < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "batch < 0");
+  if (c->batch > 65535) return fail(SINK_ATTN_UNSUPPORTED, "batch > 65535");
+  if (c->n_sink < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "n_sink < 0");
+  if (c->window < 1) return fail(SINK_ATTN_INVALID_ARGUMENT, "window < 1");
+  if (c->num_kv_heads < 1) return fail(SINK_ATTN_INVALID_ARGUMENT, "num_kv_heads < 1");
+  if (c->head_dim < 8 || c->head_dim > SINK_ATTN_MAX_HEAD_DIM || c->head_dim % 8 != 0)
+    return fail(SINK_ATTN_UNSUPPORTED, "head_dim %d not supported", c->head_dim);
+  if (c->quantized != 0 && c->quantized != 1)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "quantized must be 0 or 1");
+  if (c->quantized && c->head_dim != 128)
+    return fail(SINK_ATTN_UNSUPPORTED, "the 8-bit cache needs head_dim 128");
+  if (static_cast<long long>(c->n_sink) + c->window > (1LL << 30))
+    return fail(SINK_ATTN_UNSUPPORTED, "n_sink + window too large");
+  const bool need = c->batch > 0;
+  if (!c->quantized) {
+    SA_TRY(check_ptr(c->k, "cache k", 16, need));
+    SA_TRY(check_ptr(c->v, "cache v", 16, need));
+  } else {
+    SA_TRY(check_ptr(c->sink_k, "sink_k", 16, need && c->n_sink > 0));
+    SA_TRY(check_ptr(c->sink_v, "sink_v", 16, need && c->n_sink > 0));
+    SA_TRY(check_ptr(c->win_k, "win_k", 16, need));
+    SA_TRY(check_ptr(c->win_v, "win_v", 16, need));
+    SA_TRY(check_ptr(c->win_k_scale, "win_k_scale", 4, need));
+    SA_TRY(check_ptr(c->win_v_scale, "win_v_scale", 4, need));
+  }
+  return SINK_ATTN_OK;
+}
+
+sa::KvCache to_kvcache(const sink_attn_kvcache_desc* c) {
+  sa::KvCache k;
+  k.batch = c->batch;
+  k.n_sink = c->n_sink;
+  k.window = c->window;
+  k.hkv = c->num_kv_heads;
+  k.d = c->head_dim;
+  k.quantized = c->quantized;
+  k.k = c->k;
+  k.v = c->v;
+  k.sink_k = c->sink_k;
+  k.sink_v = c->sink_v;
+  k.win_k = static_cast<uint8_t*>(c->win_k);
+  k.win_v = static_cast<uint8_t*>(c->win_v);
+  k.win_k_scale = c->win_k_scale;
+  k.win_v_scale = c->win_v_scale;
+  return k;
+}
+
+// The decode problem of a cache decode call (splits resolved).
+sa::Decode kvcache_decode_problem(const sink_attn_kvcache_desc* c, int32_t hq,
+                                  const int32_t* n_tokens, float scale, const float* sink,
+                                  int32_t num_splits) {
+  sa::Decode p;
+  p.cache_seqlens = n_tokens;
+  p.batch = c->batch;
+  p.slots = c->n_sink + c->window;
+  p.hq = hq;
+  p.hkv = c->num_kv_heads;
+  p.d = c->head_dim;
+  p.dtype = SINK_ATTN_BF16;
+  p.scale = scale;
+  p.sink = sink;
+  p.splits = num_splits;
+  if (p.splits == 0)
+    p.splits = c->quantized ? sa::kvcache_q8_auto_splits(p, to_kvcache(c)) : sa::decode_auto_splits(p);
+  if (p.splits > p.slots && p.slots > 0) p.splits = p.slots;
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -400,6 +471,86 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     return hip_status(e, "sink_attn_bwd launch");
   } catch (...) {
     return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_bwd");
+  }
+}
+
+int sink_attn_check_kvcache_append(const sink_attn_kvcache_desc* cache, const void* k_new,
+                                   const void* v_new, int32_t chunk, const int32_t* n_seen) {
+  SA_TRY(check_kvcache_desc(cache));
+  if (chunk < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "chunk < 0");
+  const long long rows = static_cast<long long>(cache->batch) * chunk * cache->num_kv_heads;
+  if (rows > 0x7fffffffLL) return fail(SINK_ATTN_UNSUPPORTED, "batch * chunk * num_kv_heads too large");
+  const bool need = rows > 0;
+  SA_TRY(check_ptr(k_new, "k_new", 16, need));
+  SA_TRY(check_ptr(v_new, "v_new", 16, need));
+  SA_TRY(check_ptr(n_seen, "n_seen", 4, need));
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_kvcache_append(const sink_attn_kvcache_desc* cache, const void* k_new,
+                             const void* v_new, int32_t chunk, const int32_t* n_seen, void* stream) {
+  try {
+    SA_TRY(sink_attn_check_kvcache_append(cache, k_new, v_new, chunk, n_seen));
+    if (static_cast<long long>(cache->batch) * chunk == 0) return SINK_ATTN_OK;
+    hipError_t e = sa::launch_kvcache_append(to_kvcache(cache), k_new, v_new, chunk, n_seen,
+                                             static_cast<hipStream_t>(stream));
+    return hip_status(e, "sink_attn_kvcache_append launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_kvcache_append");
+  }
+}
+
+size_t sink_attn_kvcache_decode_workspace_size(const sink_attn_kvcache_desc* cache,
+                                               int32_t num_q_heads, int32_t num_splits) {
+  if (check_kvcache_desc(cache) != SINK_ATTN_OK || num_q_heads < 1 || num_splits < 0) return 0;
+  const sa::Decode p = kvcache_decode_problem(cache, num_q_heads, nullptr, 1.f, nullptr, num_splits);
+  if (!cache->quantized) return decode_ws_bytes(p);
+  return p.splits > 1 ? round_up(static_cast<size_t>(p.batch) * p.hq * p.splits * (p.d + 2) * 4) : 0;
+}
+
+int sink_attn_check_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
+                                   int32_t num_q_heads, const int32_t* n_tokens, float softmax_scale,
+                                   int32_t num_splits, const void* o, const float* lse, const float* s,
+                                   size_t workspace_bytes) {
+  SA_TRY(check_kvcache_desc(cache));
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (num_q_heads > 65535) return fail(SINK_ATTN_UNSUPPORTED, "num_q_heads > 65535");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  if (num_splits < 0 || num_splits > 256)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "num_splits must be in [0, 256]");
+  const bool need = cache->batch > 0;
+  SA_TRY(check_ptr(q, "q", 16, need));
+  SA_TRY(check_ptr(n_tokens, "n_tokens", 4, need));
+  SA_TRY(check_ptr(o, "o", 16, need));
+  SA_TRY(check_ptr(lse, "lse", 4, need));
+  SA_TRY(check_ptr(s, "s", 4, false));
+  const size_t ws = sink_attn_kvcache_decode_workspace_size(cache, num_q_heads, num_splits);
+  if (workspace_bytes < ws)
+    return fail(SINK_ATTN_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu", workspace_bytes, ws);
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q, int32_t num_q_heads,
+                             const int32_t* n_tokens, float softmax_scale,
+                             const float* learnable_sink, int32_t num_splits, void* o, float* lse,
+                             float* s, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    SA_TRY(sink_attn_check_kvcache_decode(cache, q, num_q_heads, n_tokens, softmax_scale, num_splits,
+                                          o, lse, s, workspace_bytes));
+    SA_TRY(check_ptr(learnable_sink, "learnable_sink", 4, false));
+    if (cache->batch == 0) return SINK_ATTN_OK;
+    const sa::Decode p = kvcache_decode_problem(cache, num_q_heads, n_tokens, softmax_scale,
+                                                learnable_sink, num_splits);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    hipError_t e = cache->quantized
+                       ? sa::launch_kvcache_decode_q8(p, to_kvcache(cache), q, o, lse, s, ws, st)
+                       : sa::launch_decode(p, q, cache->k, cache->v, o, lse, s, ws, st);
+    return hip_status(e, "sink_attn_kvcache_decode launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_kvcache_decode");
   }
 }
 

@@ -231,6 +231,52 @@ def make_decode(name: str, batch: int, slots: int, hq: int, hkv: int, d: int,
                   sink=a, scale=1.0 / float(np.sqrt(d)))
 
 
+@dataclasses.dataclass
+class KvDecodeQ8:
+    """A filled 8-bit rolling cache and one query per sequence.  The ring
+    holds e4m3 codes drawn directly (uniform over the 254 non-NaN codes) with
+    per-(sequence, KV head, slot) scales near those of unit-normal rows; no
+    quantisation is computed here."""
+    batch: int
+    n_sink: int
+    window: int
+    hq: int
+    hkv: int
+    d: int
+    q: np.ndarray            # float32 (bf16-exact) [B, Hq, D]
+    sink_k: np.ndarray       # float32 (bf16-exact) [B, n_sink, Hkv, D]
+    sink_v: np.ndarray
+    win_k: np.ndarray        # uint8 [B, window, Hkv, D]
+    win_v: np.ndarray
+    win_k_scale: np.ndarray  # float32 [B, Hkv, window]
+    win_v_scale: np.ndarray
+    n_tokens: np.ndarray     # int32 [B]: stream lengths (>= n_sink + window: full caches)
+    sink: np.ndarray         # float32 [Hq]
+    scale: float
+
+
+def kvcache_q8_decode(batch: int = 128, n_sink: int = 4, window: int = 4092, hq: int = 64,
+                      hkv: int = 8, d: int = 128, seed: int = 0) -> KvDecodeQ8:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    valid = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+
+    def codes(shape):
+        return valid[rng.integers(0, len(valid), size=shape, dtype=np.uint8)]
+
+    def scales(shape):
+        return (rng.uniform(2.0, 4.0, size=shape) / 448.0).astype(np.float32)
+
+    q = _draw(rng, (batch, hq, d), "bf16").f32
+    sk = _draw(rng, (batch, n_sink, hkv, d), "bf16").f32
+    sv = _draw(rng, (batch, n_sink, hkv, d), "bf16").f32
+    wk, wv = codes((batch, window, hkv, d)), codes((batch, window, hkv, d))
+    ks, vs = scales((batch, hkv, window)), scales((batch, hkv, window))
+    n_tokens = rng.integers(n_sink + window, 4 * (n_sink + window), size=batch).astype(np.int32)
+    a = rng.standard_normal(size=hq, dtype=np.float32)
+    return KvDecodeQ8(batch, n_sink, window, hq, hkv, d, q, sk, sv, wk, wv, ks, vs, n_tokens, a,
+                      1.0 / float(np.sqrt(d)))
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------

@@ -1,0 +1,138 @@
+"""GPU parity of the rolling KV cache ("What is Attention Sink? ...
+StreamingLLM" (model.playoffer.cn), core idea and engineering notes;
+"Attention Sink" (lijianxiong.space), H2O circular queue): appends bit for bit
+against the oracle's placement and 8-bit quantisation, and decode over the
+bf16 and the 8-bit cache against the oracle's decode of the same slots."""
+import numpy as np
+import pytest
+import torch
+
+import streamingllm_sink_attn_amd as sa
+from oracle import kvcache_oracle as KO
+from streamingllm_sink_attn_amd import workloads as W
+
+from gpu_helpers import DEV, TOL_BF16, assert_lse, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(rng, shape, scale=1.0):
+    """bf16-exact float32 values and the matching device tensor."""
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    t = torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+    return t.float().cpu().numpy(), t
+
+
+def _state(cache):
+    """Device cache arrays as numpy (bf16 as float32)."""
+    if not cache.quantized:
+        return dict(k=host(cache.k.float()), v=host(cache.v.float()))
+    return dict(sink_k=host(cache.sink_k.float()), sink_v=host(cache.sink_v.float()),
+                win_k=host(cache.win_k), win_v=host(cache.win_v),
+                win_k_scale=host(cache.win_k_scale), win_v_scale=host(cache.win_v_scale))
+
+
+def _stream(rng, B, hkv, d, n_sink, window, quantized, chunks, start=None, kscale=1.0):
+    """Append the chunks on the GPU and in the oracle; compare after each."""
+    cache = sa.KvCache(B, n_sink, window, hkv, d, quantized)
+    ref = KO.new_cache(B, n_sink, window, hkv, d, quantized)
+    seen = np.zeros(B, np.int32) if start is None else np.array(start, np.int32)
+    toks = []
+    for c in chunks:
+        k, kt = _bf16(rng, (B, c, hkv, d), kscale)
+        v, vt = _bf16(rng, (B, c, hkv, d))
+        sa.kvcache_append(cache, kt, vt, torch.from_numpy(seen).to(DEV))
+        torch.cuda.synchronize()
+        KO.append(ref, k, v, seen, n_sink, window)
+        got = _state(cache)
+        for key, want in ref.items():
+            if key == "quantized":
+                continue
+            assert np.array_equal(got[key], want), f"{key} differs after chunk {c}"
+        seen = seen + c
+        toks.append((k, v))
+    return cache, ref, seen
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+@pytest.mark.parametrize("n_sink,window,chunks", [(4, 40, [1, 7, 33, 2, 90, 1]), (0, 32, [5, 64]),
+                                                  (6, 17, [3, 3, 40])])
+def test_append_bit_exact(quantized, n_sink, window, chunks):
+    print(f"[case] kvcache append q={quantized} {n_sink} {window} {chunks}", flush=True)
+    rng = np.random.default_rng(11)
+    _stream(rng, 3, 2, 128, n_sink, window, quantized, chunks, kscale=3.0)
+
+
+def test_append_small_head_dim_and_offset_streams():
+    """bf16 layout with D = 64 and sequences at different stream positions."""
+    print("[case] kvcache append d64 offsets", flush=True)
+    rng = np.random.default_rng(12)
+    _stream(rng, 4, 1, 64, 4, 20, False, [5, 30, 2], start=[0, 3, 100, 17])
+
+
+def _check_decode(cache, ref, seen, n_sink, window, hq, splits, rng, sink=True):
+    B = cache.batch
+    q, qt = _bf16(rng, (B, hq, cache.d))
+    a = rng.standard_normal(hq).astype(np.float32) if sink else None
+    at = torch.from_numpy(a).to(DEV) if sink else None
+    nt = torch.from_numpy(np.asarray(seen, np.int32)).to(DEV)
+    o, lse, s = sa.kvcache_decode(cache, qt, nt, 0.11, at, num_splits=splits)
+    torch.cuda.synchronize()
+    ro, rl, rs = KO.cache_decode(q, ref, seen, n_sink, window, 0.11, sink=a)
+    err = np.abs(host(o.float()) - ro)
+    assert err.max() <= TOL_BF16["o_max"], f"O max err {err.max():.3e}"
+    assert err.mean() <= TOL_BF16["o_mean"]
+    assert_lse(host(lse), rl, TOL_BF16["lse"])
+    assert np.max(np.abs(host(s) - rs)) <= TOL_BF16["s"]
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_over_cache(quantized, splits):
+    print(f"[case] kvcache decode q={quantized} splits={splits}", flush=True)
+    rng = np.random.default_rng(13)
+    n_sink, window = 4, 300
+    # fill levels: first tokens only, a partly filled ring, a wrapped ring
+    for chunks in ([3], [3, 40], [3, 40, 280, 150]):
+        cache, ref, seen = _stream(rng, 4, 2, 128, n_sink, window, quantized, chunks)
+        _check_decode(cache, ref, seen, n_sink, window, 16, splits, rng)
+    # shorter streams than written: the valid slots are the first
+    # min(n, n_sink) first-token slots and the first ring slots
+    _check_decode(cache, ref, np.array([2, 4, 10, 200], np.int32), n_sink, window, 16, splits, rng,
+                  sink=False)
+
+
+@pytest.mark.timeout(600)
+def test_decode_q8_fullsize_sampled():
+    """128 sequences x (4 first tokens + 4092-token 8-bit ring), Hq=64,
+    Hkv=8: the bench workload, filled with random codes and scales, checked
+    on sampled sequences against the oracle's decode of the dequantised
+    slots."""
+    print("[case] kvcache q8 fullsize", flush=True)
+    B, n_sink, window, hq, hkv, d = 128, 4, 4092, 64, 8, 128
+    wl = W.kvcache_q8_decode(B, n_sink, window, hq, hkv, d, seed=3)
+    cache = sa.KvCache(B, n_sink, window, hkv, d, quantized=True)
+    cache.sink_k.copy_(torch.from_numpy(wl.sink_k).to(torch.bfloat16))
+    cache.sink_v.copy_(torch.from_numpy(wl.sink_v).to(torch.bfloat16))
+    cache.win_k.copy_(torch.from_numpy(wl.win_k))
+    cache.win_v.copy_(torch.from_numpy(wl.win_v))
+    cache.win_k_scale.copy_(torch.from_numpy(wl.win_k_scale))
+    cache.win_v_scale.copy_(torch.from_numpy(wl.win_v_scale))
+    qt = torch.from_numpy(wl.q).to(DEV).to(torch.bfloat16)
+    nt = torch.from_numpy(wl.n_tokens).to(DEV)
+    at = torch.from_numpy(wl.sink).to(DEV)
+    o, lse, s = sa.kvcache_decode(cache, qt, nt, wl.scale, at)
+    torch.cuda.synchronize()
+    ho, hl, hs = host(o.float()), host(lse), host(s)
+    q = qt.float().cpu().numpy()
+    for b in (0, 1, 77, 127):
+        one = {key: (val[b:b + 1] if isinstance(val, np.ndarray) else val)
+               for key, val in dict(quantized=True, sink_k=wl.sink_k, sink_v=wl.sink_v, win_k=wl.win_k,
+                                    win_v=wl.win_v, win_k_scale=wl.win_k_scale,
+                                    win_v_scale=wl.win_v_scale).items()}
+        ro, rl, rs = KO.cache_decode(q[b:b + 1], one, wl.n_tokens[b:b + 1], n_sink, window, wl.scale,
+                                     sink=wl.sink)
+        err = np.abs(ho[b] - ro[0])
+        assert err.max() <= TOL_BF16["o_max"], f"seq {b}: O max err {err.max():.3e}"
+        assert_lse(hl[b], rl[0], TOL_BF16["lse"])
+        assert np.max(np.abs(hs[b] - rs[0])) <= TOL_BF16["s"]
