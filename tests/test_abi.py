@@ -174,3 +174,52 @@ def test_check_fwd_gated_and_head_importance():
     assert chk_i(10, 0) == B.INVALID_ARGUMENT
     assert chk_i(10, 4, imp=None) == B.INVALID_ARGUMENT
     assert chk_i(10, 4, gate=FAKE + 1) == B.INVALID_ARGUMENT
+
+
+def _kdesc(**kw):
+    d = dict(batch=4, n_sink=4, window=100, num_kv_heads=2, head_dim=128, quantized=0, k=FAKE,
+             v=FAKE, sink_k=None, sink_v=None, win_k=None, win_v=None, win_k_scale=None,
+             win_v_scale=None)
+    d.update(kw)
+    return B.KvCacheDesc(**d)
+
+
+_Q8 = dict(quantized=1, k=None, v=None, sink_k=FAKE, sink_v=FAKE, win_k=FAKE, win_v=FAKE,
+           win_k_scale=FAKE, win_v_scale=FAKE)
+
+
+def test_check_kvcache_append_and_decode():
+    L = B.lib()
+
+    def app(desc, chunk=8, k=FAKE, v=FAKE, n=FAKE):
+        return L.sink_attn_check_kvcache_append(ctypes.byref(desc), k, v, chunk, n)
+
+    def dec(desc, hq=8, n=FAKE, scale=0.1, splits=0, q=FAKE, o=FAKE, lse=FAKE, s=None, ws=None):
+        if ws is None:
+            ws = L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(desc), hq, splits)
+        return L.sink_attn_check_kvcache_decode(ctypes.byref(desc), q, hq, n, scale, splits, o, lse, s,
+                                                ws)
+    assert app(_kdesc()) == B.OK and app(_kdesc(**_Q8)) == B.OK
+    assert app(_kdesc(), chunk=0, k=None, v=None, n=None) == B.OK        # nothing to append
+    assert app(_kdesc(), chunk=-1) == B.INVALID_ARGUMENT
+    assert app(_kdesc(), n=None) == B.INVALID_ARGUMENT
+    assert app(_kdesc(window=0)) == B.INVALID_ARGUMENT
+    assert app(_kdesc(n_sink=-1)) == B.INVALID_ARGUMENT
+    assert app(_kdesc(quantized=2)) == B.INVALID_ARGUMENT
+    assert app(_kdesc(head_dim=64)) == B.OK                                 # bf16 layout: any D
+    assert app(_kdesc(head_dim=64, **_Q8)) == B.UNSUPPORTED                 # 8-bit ring: D = 128
+    assert app(_kdesc(k=None)) == B.INVALID_ARGUMENT                        # bf16 layout needs k, v
+    assert app(_kdesc(**dict(_Q8, win_k_scale=None))) == B.INVALID_ARGUMENT
+    assert app(_kdesc(**dict(_Q8, n_sink=0, sink_k=None, sink_v=None))) == B.OK
+    assert app(_kdesc(**dict(_Q8, win_k=FAKE + 8))) == B.INVALID_ARGUMENT   # misaligned
+    assert dec(_kdesc()) == B.OK and dec(_kdesc(**_Q8)) == B.OK
+    assert dec(_kdesc(), hq=5) == B.INVALID_ARGUMENT                        # not a multiple of Hkv
+    assert dec(_kdesc(), n=None) == B.INVALID_ARGUMENT
+    assert dec(_kdesc(), scale=0.0) == B.INVALID_ARGUMENT
+    assert dec(_kdesc(), splits=300) == B.INVALID_ARGUMENT
+    for q8 in ({}, _Q8):
+        need = L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(_kdesc(**q8)), 8, 4)
+        assert need >= 4 * 8 * 4 * 130 * 4                                  # B * Hq * splits * (D + 2)
+        assert dec(_kdesc(**q8), splits=4, ws=need - 1) == B.WORKSPACE_TOO_SMALL
+    # one split on the 8-bit ring: no partials, no workspace
+    assert L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(_kdesc(**_Q8)), 8, 1) == 0
