@@ -177,7 +177,8 @@ typedef struct sink_attn_decode_desc {
  *                               is code * scale, with scale = amax / 448 and
  *                               code = e4m3(x * (448 / amax)) rounded to
  *                               nearest even (a zero row: scale 0, codes 0).
- * All pointers are device memory owned by the caller; unused ones may be NULL.
+ * All pointers are device memory owned by the caller, 16-byte aligned;
+ * unused ones may be NULL.
  */
 typedef struct sink_attn_kvcache_desc {
   int32_t batch;

@@ -84,6 +84,16 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                fp8x2_to_bf16x2(w1, true)};
 }
 
+// First of the 8 dims that quarter gq holds at k-step ks.  bf16 cache: dims
+// ks*32 + gq*8, so the four quarters of a slot read 64 contiguous bytes per
+// k-step.  8-bit cache: (ks/2)*64 + gq*16 + (ks%2)*8, so one 16-byte load
+// brings two k-steps of e4m3 codes and the four quarters read 64 contiguous
+// bytes of the row per load.
+template <bool Q8>
+__device__ __forceinline__ int kdim(int ks, int gq) {
+  return Q8 ? (ks >> 1) * 64 + gq * 16 + (ks & 1) * 8 : ks * 32 + gq * 8;
+}
+
 template <bool Q8>
 __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
                                                        const uint16_t* __restrict__ Q,
@@ -130,14 +140,16 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
   const int l16 = lane & 15;
   const int gq = lane >> 4;
 
-  // Q^T as B operand: lane (head l16, quarter gq), k-step ks: dims ks*32 + gq*8.
+  // Q^T as B operand: lane (head l16, quarter gq) holds at k-step ks the 8
+  // dims kdim(ks, gq) (K uses the same order, so the sum over k-steps is the
+  // full dot product whatever the order).
   bf16x8 qf[4];
   {
     const bool ok = l16 < nh;
-    const uint16_t* src = Q + (static_cast<size_t>(b) * p.hq + h0 + (ok ? l16 : 0)) * D + gq * 8;
+    const uint16_t* src = Q + (static_cast<size_t>(b) * p.hq + h0 + (ok ? l16 : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qf[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 32))
+      qf[ks] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + kdim<Q8>(ks, gq)))
                   : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
@@ -169,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
   float ksc[8], vsc[8], ksn[8], vsn[8];
   const int ring_last = Q8 ? max(qc.window - 1, 0) : 0;
   const int sink_last = Q8 ? max(ns - 1, 0) : 0;
+  const bool sc_vec = Q8 && (qc.window & 3) == 0;   // scale rows in whole 16-byte groups
 
   auto load_k = [&](int cs, u32x4 (&dst)[2][4]) {
     if constexpr (Q8) {
@@ -176,21 +189,35 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const int r = min(cs - ns_pad + mt * 16 + l16, ring_last);
-          const uint8_t* src = Kw + static_cast<size_t>(r) * row_stride + gq * 8;
+          const uint8_t* src = Kw + static_cast<size_t>(r) * row_stride + gq * 16;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(src + ks * 32);
-            dst[mt][ks] = u32x4{w[0], w[1], 0u, 0u};
+          for (int j = 0; j < 2; ++j) {              // k-steps 2j, 2j+1
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + j * 64);
+            dst[mt][2 * j] = u32x4{w[0], w[1], 0u, 0u};
+            dst[mt][2 * j + 1] = u32x4{w[2], w[3], 0u, 0u};
           }
         }
+        if (sc_vec) {
+          // 4 consecutive slots per load; a start past the ring (only slots
+          // that the mask drops) reads the ring's last 4 scales instead.
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < 2; ++mt) {
+            const int r = min(cs - ns_pad + 16 * mt + 4 * gq, qc.window - 4);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(Ksc + r);
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(Vsc + r);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = min(cs - ns_pad + 16 * mt + 4 * gq + i, ring_last);
-            ksn[mt * 4 + i] = Ksc[r];
-            vsn[mt * 4 + i] = Vsc[r];
+            for (int i = 0; i < 4; ++i) { ksn[mt * 4 + i] = a[i]; vsn[mt * 4 + i] = bb[i]; }
           }
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = min(cs - ns_pad + 16 * mt + 4 * gq + i, ring_last);
+              ksn[mt * 4 + i] = Ksc[r];
+              vsn[mt * 4 + i] = Vsc[r];
+            }
+        }
         return;
       }
     }
@@ -199,19 +226,18 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
       int slot = cs + mt * 16 + l16;
       if constexpr (Q8) slot = min(slot, sink_last);
       else slot = slot < p.slots ? slot : p.slots - 1;
-      const uint16_t* src = Kb + static_cast<size_t>(slot) * row_stride + gq * 8;
+      const uint16_t* src = Kb + static_cast<size_t>(slot) * row_stride;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = *reinterpret_cast<const u32x4*>(src + ks * 32);
+      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = *reinterpret_cast<const u32x4*>(src + kdim<Q8>(ks, gq));
     }
   };
   auto load_v = [&](int cs) {
     if constexpr (Q8) {
-      if (cs >= ns_pad) {
+      if (cs >= ns_pad) {                            // 8 lanes per 128-byte row
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = min(cs - ns_pad + (lane >> 4) + 4 * i, ring_last);
-          const u32x2 w = *reinterpret_cast<const u32x2*>(Vw + static_cast<size_t>(r) * row_stride + l16 * 8);
-          vr[i] = u32x4{w[0], w[1], 0u, 0u};
+        for (int i = 0; i < 4; ++i) {
+          const int r = min(cs - ns_pad + (lane >> 3) + 8 * i, ring_last);
+          vr[i] = *reinterpret_cast<const u32x4*>(Vw + static_cast<size_t>(r) * row_stride + (lane & 7) * 16);
         }
         return;
       }
@@ -225,15 +251,24 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
     }
   };
   auto store_v = [&](uint16_t* buf, bool win) {
+    if constexpr (Q8) {
+      if (win) {                                     // e4m3 codes -> bf16, exactly
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = (lane >> 3) + 8 * i;
+          const int c0 = (lane & 7) * 2;
+          *reinterpret_cast<u32x4*>(buf + row * D + (c0 ^ vswz(row)) * 8) = fp8x8_to_bf16x8(vr[i][0], vr[i][1]);
+          *reinterpret_cast<u32x4*>(buf + row * D + ((c0 + 1) ^ vswz(row)) * 8) =
+              fp8x8_to_bf16x8(vr[i][2], vr[i][3]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = (lane >> 4) + 4 * i;
       const int pc = l16 ^ vswz(row);
-      u32x4 x = vr[i];
-      if constexpr (Q8) {
-        if (win) x = fp8x8_to_bf16x8(x[0], x[1]);
-      }
-      *reinterpret_cast<u32x4*>(buf + row * D + pc * 8) = x;
+      *reinterpret_cast<u32x4*>(buf + row * D + pc * 8) = vr[i];
     }
   };
 
@@ -293,7 +328,20 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (cs + 16 * mt + 4 * gq + i >= lim) sacc[mt][i] = -kInf;
+          if (cs + 16 * mt + 4 * gq + i >= lim) {
+            sacc[mt][i] = -kInf;
+            if constexpr (Q8) vsc[mt * 4 + i] = 0.f;
+          }
+      // Unused slots may hold anything (NaN included) and 0 * NaN is NaN in
+      // P V: zero their V rows in this wavefront's buffer (LDS operations of
+      // one wavefront complete in order, so the reads below see the zeros).
+      uint16_t* vz = vbuf[w][cur];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = (lane >> 4) + 4 * i;
+        if (cs + row >= lim)
+          *reinterpret_cast<u32x4*>(vz + row * D + (l16 ^ vswz(row)) * 8) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     float mx = -kInf;
 #pragma unroll

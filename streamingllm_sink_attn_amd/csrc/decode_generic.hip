@@ -19,7 +19,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(Decode p, const void
   const int g = h / (p.hq / p.hkv);
   const int D = p.d;
   const int nr = (D + 63) / 64;
-  const int n = p.cache_seqlens ? p.cache_seqlens[b] : p.slots;
+  const int n = p.cache_seqlens ? min(p.cache_seqlens[b], p.slots) : p.slots;
   const size_t qrow = (static_cast<size_t>(b) * p.hq + h) * D;
 
   float qv[4], acc[4];

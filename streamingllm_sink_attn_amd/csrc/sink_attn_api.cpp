@@ -212,8 +212,8 @@ int check_kvcache_desc(const sink_attn_kvcache_desc* c) {
     SA_TRY(check_ptr(c->sink_v, "sink_v", 16, need && c->n_sink > 0));
     SA_TRY(check_ptr(c->win_k, "win_k", 16, need));
     SA_TRY(check_ptr(c->win_v, "win_v", 16, need));
-    SA_TRY(check_ptr(c->win_k_scale, "win_k_scale", 4, need));
-    SA_TRY(check_ptr(c->win_v_scale, "win_v_scale", 4, need));
+    SA_TRY(check_ptr(c->win_k_scale, "win_k_scale", 16, need));
+    SA_TRY(check_ptr(c->win_v_scale, "win_v_scale", 16, need));
   }
   return SINK_ATTN_OK;
 }

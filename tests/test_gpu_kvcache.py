@@ -102,6 +102,27 @@ def test_decode_over_cache(quantized, splits):
                   sink=False)
 
 
+@pytest.mark.parametrize("quantized", [False, True])
+def test_decode_ignores_unwritten_slots(quantized):
+    """Ring slots not yet written may hold anything: NaN codes, values and
+    scales there change nothing."""
+    print(f"[case] kvcache unwritten slots q={quantized}", flush=True)
+    rng = np.random.default_rng(14)
+    n_sink, window = 4, 300
+    cache, ref, seen = _stream(rng, 3, 2, 128, n_sink, window, quantized, [3, 40])
+    nw = int(seen[0]) - n_sink                       # ring slots written so far (same for all)
+    if not quantized:
+        cache.k[:, n_sink + nw:] = float("nan")
+        cache.v[:, n_sink + nw:] = float("nan")
+    else:
+        cache.win_k[:, nw:] = 0x7F                   # the e4m3 NaN code
+        cache.win_v[:, nw:] = 0x7F
+        cache.win_k_scale[:, :, nw:] = float("nan")
+        cache.win_v_scale[:, :, nw:] = float("inf")
+    for splits in (0, 1, 3):
+        _check_decode(cache, ref, seen, n_sink, window, 16, splits, rng)
+
+
 @pytest.mark.timeout(600)
 def test_decode_q8_fullsize_sampled():
     """128 sequences x (4 first tokens + 4092-token 8-bit ring), Hq=64,

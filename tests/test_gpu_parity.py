@@ -251,6 +251,37 @@ def test_decode_variants(name, splits):
     assert float(np.max(np.abs(host(s) - rs))) <= tol["s"]
 
 
+@pytest.mark.parametrize("name", ["d128_g4_lens", "f32"])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_ignores_unused_slots(name, splits):
+    """Slots at or past cache_seqlens may hold anything: NaN and Inf there
+    change nothing (a zero probability times NaN would be NaN)."""
+    c = dict(DECODE_CASES[name])
+    if "cache_seqlens" not in c:
+        c["cache_seqlens"] = [70, 33][:c["batch"]]
+    wl = W.make_decode(name, c.pop("batch"), c.pop("slots"), c.pop("hq"), c.pop("hkv"), c.pop("d"),
+                       seed=4, **c)
+    _announce(f"decode unused slots {name} splits={splits}")
+    q = dev(wl.q, wl.dtype)
+    kc, vc = dev(wl.k_cache, wl.dtype), dev(wl.v_cache, wl.dtype)
+    for b, n in enumerate(wl.cache_seqlens):
+        kc[b, int(n):] = float("nan")
+        vc[b, int(n):] = float("nan")
+        if int(n) + 1 < wl.slots:
+            vc[b, int(n) + 1] = float("inf")
+    csl = torch.from_numpy(wl.cache_seqlens).to(DEV)
+    sink = torch.from_numpy(wl.sink).to(DEV) if wl.sink is not None else None
+    o, lse, s = sa.decode(q, kc, vc, csl, wl.scale, sink, num_splits=splits)
+    torch.cuda.synchronize()
+    ro, rl, rs = oracle.decode(wl.q.f32, wl.k_cache.f32, wl.v_cache.f32, wl.scale,
+                               cache_seqlens=wl.cache_seqlens, sink=wl.sink)
+    tol = tol_for(wl.dtype)
+    assert np.all(np.isfinite(host(o)))
+    assert_out(host(o), ro, tol)
+    assert_lse(host(lse), rl, tol["lse"])
+    assert float(np.max(np.abs(host(s) - rs))) <= tol["s"]
+
+
 def test_decode_permutation_and_split_invariance():
     """Slots are an unordered set and the split merge is exact: permuting the
     cache or changing num_splits changes the result only by rounding."""
