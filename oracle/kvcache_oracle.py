@@ -32,6 +32,13 @@ Readings (each is listed in DESIGN.md):
   * Decode over the cache: the current token is already appended; the valid
     slots are every slot a position was written to; no causal or window mask
     beyond that (the cache content is the mask).
+  * Chunked prefill against the cache: chunk row c of a stream that has
+    appended P0 tokens is position p = P0 + c and sees key position k when
+    k <= p and (k < n_sink or p - k < W), the prefill mask of StreamingLLM
+    ([QA] core idea) over the stream; keys before P0 come from the cache as
+    it is before the chunk is appended, the others from the chunk.  The
+    8-bit ring enters as bfloat16(float32(code value) * scale), rounded to
+    nearest even: the prefill consumes bfloat16 keys and values.
 """
 from __future__ import annotations
 
@@ -41,7 +48,7 @@ from .sink_attn_oracle import decode as _decode
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_rows", "dequantize", "slot_of",
-    "new_cache", "append", "kept_positions", "cache_decode",
+    "new_cache", "append", "kept_positions", "cache_decode", "bf16_round", "cache_prefill",
 ]
 
 E4M3_MAX = 448.0
@@ -178,3 +185,60 @@ def cache_decode(q, cache, n_tokens, n_sink, window, scale, sink=None):
     n = np.asarray(n_tokens, dtype=np.int64)
     valid = np.minimum(n, n_sink) + np.minimum(np.maximum(n - n_sink, 0), window)
     return _decode(q, k, v, scale, cache_seqlens=valid, sink=sink)
+
+
+def bf16_round(x):
+    """float32 values rounded to the nearest bfloat16, ties to even (finite
+    inputs), returned as float32."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _key_at(cache, b, pos, n_sink, window):
+    """K and V rows [Hkv, D] (float64) the cache holds for stream position pos."""
+    kind, slot = slot_of(pos, n_sink, window)
+    if not cache["quantized"]:
+        i = slot if kind == "sink" else n_sink + slot
+        return np.asarray(cache["k"][b, i], np.float64), np.asarray(cache["v"][b, i], np.float64)
+    if kind == "sink":
+        return (np.asarray(cache["sink_k"][b, slot], np.float64),
+                np.asarray(cache["sink_v"][b, slot], np.float64))
+    out = []
+    for codes, sc in ((cache["win_k"][b, slot], cache["win_k_scale"][b, :, slot]),
+                      (cache["win_v"][b, slot], cache["win_v_scale"][b, :, slot])):
+        vals = e4m3_decode(codes).astype(np.float32) * np.asarray(sc, np.float32)[:, None]
+        out.append(bf16_round(vals).astype(np.float64))
+    return out[0], out[1]
+
+
+def cache_prefill(q, cache, k_new, v_new, n_seen, n_sink, window, scale, sink=None, rows=None):
+    """Chunked prefill against the cache (reading above), row by row: each
+    row's visible keys in position order, then the plain decode definition
+    on them.  q [B, C, Hq, D], k_new / v_new [B, C, Hkv, D].  Returns o [B, C,
+    Hq, D], lse and s [B, C, Hq]; with rows = [(b, c), ...] only those rows
+    (the others stay zero)."""
+    q = np.asarray(q, np.float64)
+    B, C, hq, d = q.shape
+    o = np.zeros((B, C, hq, d))
+    lse = np.zeros((B, C, hq))
+    s = np.zeros((B, C, hq))
+    todo = rows if rows is not None else [(b, c) for b in range(B) for c in range(C)]
+    for b, c in todo:
+        p0 = int(n_seen[b])
+        p = p0 + c
+        vis = [k for k in range(p + 1) if k < n_sink or p - k < window]
+        ks, vs = [], []
+        for k in vis:
+            if k < p0:
+                kk, vv = _key_at(cache, b, k, n_sink, window)
+            else:
+                kk = np.asarray(k_new[b, k - p0], np.float64)
+                vv = np.asarray(v_new[b, k - p0], np.float64)
+            ks.append(kk)
+            vs.append(vv)
+        kd = np.stack(ks)[None]                     # [1, n_vis, Hkv, D]
+        vd = np.stack(vs)[None]
+        ro, rl, rs = _decode(q[b, c][None], kd, vd, scale, sink=sink)
+        o[b, c], lse[b, c], s[b, c] = ro[0], rl[0], rs[0]
+    return o, lse, s

@@ -149,3 +149,117 @@ def test_quantized_cache_decode_is_decode_of_dequantized_values():
     o_b, _, _ = KO.cache_decode(q, bc, n, n_sink, window, 0.2)
     np.testing.assert_array_equal(o_q[0], o_b[0])
     assert np.max(np.abs(o_q - o_b)) < 0.1
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill against the cache
+# ---------------------------------------------------------------------------
+
+def test_bf16_round_ties_and_library():
+    import torch
+    one = np.float32(1.0)
+    assert KO.bf16_round(np.float32(1 + 2.0 ** -8)) == one                    # tie -> even
+    assert KO.bf16_round(np.float32(1 + 3 * 2.0 ** -8)) == np.float32(1 + 2.0 ** -6)
+    assert KO.bf16_round(np.float32(1 + 2.0 ** -8 + 2.0 ** -20)) == np.float32(1 + 2.0 ** -7)
+    x = (np.random.default_rng(5).standard_normal(10000) * 100).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(KO.bf16_round(x), want)
+
+
+@pytest.mark.parametrize("n_sink,window,chunks", [(3, 20, [2, 5, 1, 30, 21, 4]), (0, 9, [4, 4, 13]),
+                                                  (4, 40, [50, 7])])
+def test_cache_prefill_equals_whole_stream_prefill(n_sink, window, chunks):
+    """Every chunk's rows, computed from the cache before the chunk is
+    appended, equal the rows of the prefill oracle over the whole stream with
+    the StreamingLLM mask: first tokens still to come, a ring still filling,
+    a wrapped ring and chunks longer than the window."""
+    rng = np.random.default_rng(6)
+    T, hq, hkv, d = sum(chunks), 4, 2, 8
+    q = rng.standard_normal((T, hq, d))
+    k = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    sink = rng.standard_normal(hq)
+    po, plse, ps = oracle.fwd(q, k, v, [0, T], 0.4, n_sink=n_sink, window=window, sink=sink)
+    cache = KO.new_cache(1, n_sink, window, hkv, d, quantized=False)
+    seen = 0
+    for c in chunks:
+        sl = slice(seen, seen + c)
+        o, lse, s = KO.cache_prefill(q[None, sl], cache, k[None, sl], v[None, sl], [seen], n_sink, window,
+                                     0.4, sink=sink)
+        np.testing.assert_allclose(o[0], po[sl], atol=1e-12)
+        np.testing.assert_allclose(lse[0], plse[sl], atol=1e-12)
+        np.testing.assert_allclose(s[0], ps[sl], atol=1e-12)
+        KO.append(cache, k[None, sl], v[None, sl], [seen], n_sink, window)
+        seen += c
+
+
+def test_cache_prefill_chunk_of_one_is_decode():
+    """A one-token chunk is a decode step: the same row as decoding over the
+    cache after appending the token."""
+    rng = np.random.default_rng(7)
+    B, hq, hkv, d, n_sink, window = 3, 4, 2, 8, 2, 6
+    for quantized in (False, True):
+        cache = KO.new_cache(B, n_sink, window, hkv, d, quantized)
+        seen = np.array([0, 3, 11])
+        for b in range(B):
+            n = int(seen[b])
+            one = {key: (val[b:b + 1] if isinstance(val, np.ndarray) else val) for key, val in cache.items()}
+            KO.append(one, rng.standard_normal((1, n, hkv, d)), rng.standard_normal((1, n, hkv, d)), [0],
+                      n_sink, window)
+        q = rng.standard_normal((B, 1, hq, d))
+        kn = rng.standard_normal((B, 1, hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((B, 1, hkv, d)).astype(np.float32)
+        if quantized:
+            kn, vn = KO.bf16_round(kn), KO.bf16_round(vn)
+        o, lse, s = KO.cache_prefill(q, cache, kn, vn, seen, n_sink, window, 0.3)
+        KO.append(cache, kn, vn, seen, n_sink, window)
+        if quantized:
+            # the decode oracle reads the exact dequantised ring; the prefill
+            # reads it rounded to bfloat16: compare on a plain cache holding
+            # the rounded values
+            plain = KO.new_cache(B, n_sink, window, hkv, d, False)
+            plain["k"][:, :n_sink] = cache["sink_k"]
+            plain["v"][:, :n_sink] = cache["sink_v"]
+            for name, sc in (("k", "win_k_scale"), ("v", "win_v_scale")):
+                deq = KO.e4m3_decode(cache["win_" + name]).astype(np.float32) * \
+                    np.swapaxes(cache[sc], 1, 2)[..., None].astype(np.float32)
+                plain[name][:, n_sink:] = KO.bf16_round(deq)
+            # the newest token is in the ring too, quantised: put its chunk value back
+            for b in range(B):
+                p = int(seen[b])
+                kind, slot = KO.slot_of(p, n_sink, window)
+                i = slot if kind == "sink" else n_sink + slot
+                plain["k"][b, i], plain["v"][b, i] = kn[b, 0], vn[b, 0]
+            cache = plain
+        do, dl, ds = KO.cache_decode(q[:, 0], cache, seen + 1, n_sink, window, 0.3)
+        np.testing.assert_allclose(o[:, 0], do, atol=1e-12)
+        np.testing.assert_allclose(lse[:, 0], dl, atol=1e-12)
+        np.testing.assert_allclose(s[:, 0], ds, atol=1e-12)
+
+
+def test_cache_prefill_q8_with_exact_values_equals_bf16():
+    """Rows whose values are e4m3 codes times a power of two (largest code
+    448) quantise without error, so the 8-bit cache prefills exactly as the
+    bf16 cache holding the same values."""
+    rng = np.random.default_rng(8)
+    B, C, hq, hkv, d, n_sink, window = 2, 5, 4, 2, 16, 2, 7
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+
+    def exact_rows(n):
+        codes = rng.choice(finite, size=(B, n, hkv, d))
+        codes[..., 0] = 0x7E                                    # amax code 448 in every row
+        return (KO.e4m3_decode(codes) * 2.0 ** rng.integers(-8, -4, size=(B, n, hkv, 1))).astype(np.float32)
+
+    qc = KO.new_cache(B, n_sink, window, hkv, d, quantized=True)
+    bc = KO.new_cache(B, n_sink, window, hkv, d, quantized=False)
+    kk, vv = exact_rows(12), exact_rows(12)
+    for c in (qc, bc):
+        KO.append(c, kk, vv, [0, 0], n_sink, window)
+    assert np.array_equal(KO.dequantize(qc["win_k"], np.swapaxes(qc["win_k_scale"], 1, 2)),
+                          bc["k"][:, n_sink:])
+    q = rng.standard_normal((B, C, hq, d))
+    kn, vn = exact_rows(C), exact_rows(C)
+    a = KO.cache_prefill(q, qc, kn, vn, [12, 12], n_sink, window, 0.25, sink=np.zeros(hq))
+    b_ = KO.cache_prefill(q, bc, kn, vn, [12, 12], n_sink, window, 0.25, sink=np.zeros(hq))
+    for x, y in zip(a, b_):
+        np.testing.assert_array_equal(x, y)
