@@ -294,6 +294,36 @@ def bench_kvcache_q8_decode(torch, sa, W, steps, warmup):
                        "hkv": H, "head_dim": D, "ring": "e4m3 + per-row float32 scales"}}
 
 
+def bench_kvcache_prefill(torch, sa, W, steps, warmup):
+    """Chunked prefill against the rolling cache: 8 streams each taking a
+    1024-token chunk against (4 first tokens + 1024-token window) bf16
+    caches, Hq=32, Hkv=8, D=128, streams past their first window.  One step is
+    the whole call (packing the cache and chunk, the forward, the copy of the
+    chunk rows); FLOPs count the kept (row, key) pairs at 4*D."""
+    wl = W.kvcache_prefill()
+    cache = sa.KvCache(wl.batch, wl.n_sink, wl.window, wl.hkv, wl.d, quantized=False)
+    cache.k.copy_(torch.from_numpy(wl.k_cache).to(torch.bfloat16))
+    cache.v.copy_(torch.from_numpy(wl.v_cache).to(torch.bfloat16))
+    dev = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)
+    q, kn, vn = dev(wl.q), dev(wl.k_new), dev(wl.v_new)
+    seen = torch.from_numpy(wl.n_seen).cuda()
+    sink = torch.from_numpy(wl.sink).cuda()
+    o = torch.empty_like(q)
+    pairs = wl.valid_pairs()
+    flops = 4.0 * wl.d * pairs
+
+    def step():
+        sa.kvcache_prefill(cache, q, kn, vn, seen, wl.scale, sink, out=o)
+
+    ms, _ = Timer(torch).run(step, steps, warmup)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "streaming_chunked_prefill", "unit": "TFLOP/s", "value": round(tf, 2),
+            "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_step": round(ms, 4),
+            "valid_pairs": pairs,
+            "config": {"batch": wl.batch, "chunk": wl.chunk, "n_sink": wl.n_sink, "window": wl.window,
+                       "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "cache": "bf16"}}
+
+
 def cpu_baseline(W, budget_s=15.0):
     """The float64 oracle on whole (sample, head) units of the same workload,
     until about budget_s seconds of CPU work; reported in TFLOP/s counted the
@@ -336,7 +366,7 @@ def main():
                          "tens of milliseconds of load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks", "gated",
-                                       "decode_q8"),
+                                       "decode_q8", "prefill_cache"),
                     default="all",
                     help="headline: only the GQA prefill forward (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -345,7 +375,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                          "multi-GPU sharding is not part of this build"}))
+                          "multi-GPU sharding is not implemented"}))
         sys.exit(2)
 
     import torch
@@ -362,7 +392,7 @@ def main():
         torch.cuda.empty_cache()
     single = {"decode": bench_decode, "streaming": bench_streaming_prefill,
               "blocks": bench_block_sparse, "gated": bench_gqa_gated,
-              "decode_q8": bench_kvcache_q8_decode}
+              "decode_q8": bench_kvcache_q8_decode, "prefill_cache": bench_kvcache_prefill}
     if args.legs in single:
         print(json.dumps(single[args.legs](torch, sa, W, args.steps, args.warmup)), flush=True)
         return
@@ -390,7 +420,7 @@ def main():
     }
     also = []
     legs = ((bench_streaming_prefill, bench_decode, bench_block_sparse, bench_gqa_gated,
-             bench_kvcache_q8_decode) if args.legs == "all" else ())
+             bench_kvcache_q8_decode, bench_kvcache_prefill) if args.legs == "all" else ())
     for fn in legs:
         try:
             also.append(fn(torch, sa, W, args.steps, args.warmup))

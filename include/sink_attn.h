@@ -230,6 +230,42 @@ int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill against the cache: a chunk of `chunk` new tokens per
+ * sequence attends, with the sink ([Notes] s1, s4), to the keys StreamingLLM
+ * keeps for each of its positions ("What is Attention Sink? ... StreamingLLM"
+ * (model.playoffer.cn), core idea: the first n_sink tokens and a sliding
+ * window of the most recent ones).  Row c of sequence b is stream position
+ * p = n_seen[b] + c and sees key position k when k <= p and (k < n_sink or
+ * p - k < window): the cached first tokens and ring tokens (as they were
+ * before this chunk) and the chunk's own earlier tokens.  This equals row p
+ * of sink_attn_fwd over the whole stream with that n_sink and window.  The
+ * 8-bit ring enters as code * scale rounded to bfloat16.
+ *   q             bfloat16 [B, chunk, num_q_heads, D].
+ *   k_new, v_new  bfloat16 [B, chunk, Hkv, D]: the chunk's keys and values.
+ *   n_seen        device int32 [B] (>= 0): tokens the cache has taken so far.
+ *   o             output bfloat16 [B, chunk, num_q_heads, D]; lse, s float32
+ *                 [B, chunk, num_q_heads] as sink_attn_fwd (s may be NULL).
+ *   workspace     sink_attn_kvcache_prefill_workspace_size bytes, 256-byte
+ *                 aligned (the per-sequence packed samples: B x (n_sink +
+ *                 window + chunk) rows of K, V, Q and O).
+ * The cache is read, not written: append the chunk afterwards with
+ * sink_attn_kvcache_append and the same n_seen (appending first could evict
+ * ring tokens the chunk's earlier rows still see).
+ */
+size_t sink_attn_kvcache_prefill_workspace_size(const sink_attn_kvcache_desc* cache, int32_t chunk,
+                                                int32_t num_q_heads);
+int sink_attn_check_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q,
+                                    int32_t num_q_heads, const void* k_new, const void* v_new,
+                                    int32_t chunk, const int32_t* n_seen, float softmax_scale,
+                                    const void* o, const float* lse, const float* s,
+                                    size_t workspace_bytes);
+int sink_attn_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q, int32_t num_q_heads,
+                              const void* k_new, const void* v_new, int32_t chunk,
+                              const int32_t* n_seen, float softmax_scale, const float* learnable_sink,
+                              void* o, float* lse, float* s, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Forward.  [Notes] s1 (scores, probabilities, output) and s4 (the sink as an
  * output scale).
  *   q, k, v   inputs (layouts above).

@@ -5,8 +5,8 @@ in ``include/sink_attn.h``); :mod:`.binding` marshals torch tensors into it.
 :mod:`.workloads` draws the seeded synthetic inputs.
 """
 from .binding import (KvCache, SinkAttnError, bwd, debug_visit_map, decode, fwd,  # noqa: F401
-                      fwd_gated, head_importance, kvcache_append, kvcache_decode, lib,
+                      fwd_gated, head_importance, kvcache_append, kvcache_decode, kvcache_prefill, lib,
                       prefill_path)
 
 __all__ = ["fwd", "fwd_gated", "head_importance", "bwd", "decode", "KvCache", "kvcache_append",
-           "kvcache_decode", "debug_visit_map", "prefill_path", "lib", "SinkAttnError"]
+           "kvcache_decode", "kvcache_prefill", "debug_visit_map", "prefill_path", "lib", "SinkAttnError"]

@@ -100,6 +100,11 @@ _SIGS = {
     "sink_attn_kvcache_decode": (c_i32, [c_vp, c_vp, c_i32, c_vp, ctypes.c_float, c_vp, c_i32, c_vp,
                                          c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "sink_attn_kvcache_decode_workspace_size": (ctypes.c_size_t, [c_vp, c_i32, c_i32]),
+    "sink_attn_kvcache_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, ctypes.c_float, c_vp,
+                                          c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_kvcache_prefill_workspace_size": (ctypes.c_size_t, [c_vp, c_i32, c_i32]),
+    "sink_attn_check_kvcache_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, ctypes.c_float,
+                                                c_vp, c_vp, c_vp, ctypes.c_size_t]),
     "sink_attn_check_kvcache_append": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp]),
     "sink_attn_check_kvcache_decode": (c_i32, [c_vp, c_vp, c_i32, c_vp, ctypes.c_float, c_i32, c_vp,
                                                c_vp, c_vp, ctypes.c_size_t]),
@@ -368,6 +373,31 @@ def kvcache_decode(cache: KvCache, q, n_tokens, softmax_scale=None, learnable_si
     _check(L.sink_attn_kvcache_decode(ctypes.byref(desc), _p(q), hq, _p(n_tokens), float(scale),
                                       _p(learnable_sink), int(num_splits), _p(o), _p(lse), _p(s),
                                       _p(ws), ws_bytes, _stream(stream)))
+    return o, lse, s
+
+
+def kvcache_prefill(cache: KvCache, q, k_new, v_new, n_seen, softmax_scale=None, learnable_sink=None,
+                    return_s=True, out=None, stream=None):
+    """Chunked prefill against the cache: q [B, C, Hq, D] at stream positions
+    n_seen[b] + c attends to the kept first tokens, the window (cache as it is
+    before this chunk) and the chunk itself.  The cache is not written: call
+    kvcache_append(cache, k_new, v_new, n_seen) afterwards.  Returns (o [B, C,
+    Hq, D], lse [B, C, Hq], s or None)."""
+    _need_cuda(q, k_new, v_new, n_seen, learnable_sink)
+    if n_seen.dtype != torch.int32:
+        raise SinkAttnError(INVALID_ARGUMENT, "n_seen must be int32")
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    B, C, hq, _ = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    lse = torch.empty((B, C, hq), dtype=torch.float32, device=q.device)
+    s = torch.empty((B, C, hq), dtype=torch.float32, device=q.device) if return_s else None
+    desc = cache.desc()
+    L = lib()
+    ws_bytes = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(desc), C, hq)
+    ws = _workspace(ws_bytes, q.device)
+    _check(L.sink_attn_kvcache_prefill(ctypes.byref(desc), _p(q), hq, _p(k_new), _p(v_new), C, _p(n_seen),
+                                       float(scale), _p(learnable_sink), _p(o), _p(lse), _p(s), _p(ws),
+                                       ws_bytes, _stream(stream)))
     return o, lse, s
 
 

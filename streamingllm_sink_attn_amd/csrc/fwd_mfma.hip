@@ -89,6 +89,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   const int L = p.cu[wc.b + 1] - t0;
   const int p0 = wc.pt * geo.P;
   if (p0 >= L) return;                               // uniform over the workgroup
+  if (p.qstart != nullptr && p0 + geo.P <= p.qstart[wc.b]) return;
   const int p1 = min(L, p0 + geo.P);
 
   const int tid = threadIdx.x;

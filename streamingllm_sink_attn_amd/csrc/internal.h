@@ -21,6 +21,9 @@ struct Prefill {
   const int32_t* blocks;      // [nqb, hkv, max_blocks] or nullptr
   int nqb, max_blocks;
   const float* sink;          // [hq] or nullptr
+  // [batch] or nullptr: rows before qstart[b] of sample b are not needed
+  // (a workgroup whose rows all lie before it exits; the forward only).
+  const int32_t* qstart = nullptr;
 };
 
 // Backward workspace carve-up (float32 unless noted).
@@ -102,6 +105,16 @@ hipError_t launch_visit_map(const Prefill& p, uint8_t* out, hipStream_t st);
 
 // Append `chunk` tokens per sequence (k_new, v_new bf16 [B, chunk, Hkv, D],
 // stream positions n_seen[b] + c) into the cache.
+// Chunked prefill against the cache: the packed per-sequence samples (K, V,
+// Q rows; cu of 2*batch + 1 entries, qstart of 2*batch) and the copy of the
+// chunk rows' outputs back to [batch, chunk, ...] order.
+hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const void* k_new,
+                                         const void* v_new, int chunk, int hq, const int32_t* n_seen,
+                                         int lmax, void* kp, void* vp, void* qp, int32_t* cu,
+                                         int32_t* qstart, hipStream_t st);
+hipError_t launch_kvcache_prefill_scatter(const KvCache& c, int chunk, int hq, const int32_t* n_seen,
+                                          int lmax, const void* op, const float* lsep, const float* sp,
+                                          void* o, float* lse, float* s, hipStream_t st);
 hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void* v_new, int chunk,
                                  const int32_t* n_seen, hipStream_t st);
 // Decode over the 8-bit cache: p.cache_seqlens holds the tokens appended so

@@ -92,6 +92,156 @@ __global__ __launch_bounds__(64) void append_kernel(KvCache c, const uint16_t* _
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Chunked prefill against the cache.  Query row c of sequence b is stream
+// position P0 + c (P0 = n_seen[b], the tokens the cache has taken so far); it
+// sees the keys StreamingLLM keeps for that position: the first n_sink tokens
+// and the positions within the window, from the cache (before this chunk is
+// appended) and from the chunk itself, causally.  Each sequence is laid out
+// as one packed sample of the prefill forward:
+//   [ns cached first tokens | nw ring tokens in position order | C chunk tokens]
+// (ns = min(P0, n_sink), nw = min(max(P0 - n_sink, 0), window)).  Local index
+// differences then equal position differences for every key the window can
+// reach and the first-token keys keep local index = position, so the prefill
+// mask of that sample is the StreamingLLM mask of the stream.  Sequence b owns
+// rows [b*Lmax, (b+1)*Lmax), Lmax = n_sink + window + C: the sample, then a
+// padding sample for the rest of the segment whose rows all lie before its
+// qstart (the forward skips them).
+// ---------------------------------------------------------------------------
+struct Seg {
+  int ns, nw, L;
+};
+__device__ __forceinline__ Seg segment(const KvCache& c, int p0, int chunk) {
+  Seg s;
+  p0 = max(p0, 0);                                    // negative counts read as an empty stream
+  s.ns = min(p0, c.n_sink);
+  s.nw = min(max(p0 - c.n_sink, 0), c.window);
+  s.L = s.ns + s.nw + chunk;
+  return s;
+}
+
+// 16 lanes per (sequence b, segment row i, KV head g): the K and V row of the
+// key at row i (cache or chunk) and, for chunk rows, the G query rows.
+// Also writes the samples' bounds (cu: 2B + 1, qstart: 2B).
+template <bool QUANT>
+__global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k_new,
+                                                             const uint16_t* __restrict__ v_new, int chunk,
+                                                             int hq, const int32_t* __restrict__ n_seen,
+                                                             int lmax, uint16_t* __restrict__ kp,
+                                                             uint16_t* __restrict__ vp,
+                                                             uint16_t* __restrict__ qp, int32_t* __restrict__ cu,
+                                                             int32_t* __restrict__ qstart) {
+  const size_t unit = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const size_t units = static_cast<size_t>(c.batch) * lmax * c.hkv;
+  if (unit >= units) return;
+  const int g = static_cast<int>(unit % c.hkv);
+  const int i = static_cast<int>((unit / c.hkv) % lmax);
+  const int b = static_cast<int>(unit / (static_cast<size_t>(c.hkv) * lmax));
+  const int D = c.d;
+  const int p0 = n_seen[b];
+  const Seg sg = segment(c, p0, chunk);
+  if (i == 0 && g == 0 && sub == 0) {
+    cu[2 * b] = b * lmax;
+    cu[2 * b + 1] = b * lmax + sg.L;
+    qstart[2 * b] = sg.L - chunk;
+    qstart[2 * b + 1] = lmax - sg.L;
+    if (b == c.batch - 1) cu[2 * c.batch] = c.batch * lmax;
+  }
+  if (i >= sg.L) return;
+  const size_t dst = ((static_cast<size_t>(b) * lmax + i) * c.hkv + g) * D;
+  const int nchunk8 = D / 8;                          // 16-byte pieces of a bf16 row
+  if (i >= sg.ns + sg.nw) {                           // a chunk token
+    const int cc = i - sg.ns - sg.nw;
+    const size_t src = ((static_cast<size_t>(b) * chunk + cc) * c.hkv + g) * D;
+    for (int e = sub; e < nchunk8; e += 16) {
+      *reinterpret_cast<u32x4*>(kp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
+      *reinterpret_cast<u32x4*>(vp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
+    }
+    const int G = hq / c.hkv;
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = g * G + hh;
+      const size_t qs = ((static_cast<size_t>(b) * chunk + cc) * hq + h) * D;
+      const size_t qd = ((static_cast<size_t>(b) * lmax + i) * hq + h) * D;
+      for (int e = sub; e < nchunk8; e += 16)
+        *reinterpret_cast<u32x4*>(qp + qd + 8 * e) = *reinterpret_cast<const u32x4*>(q + qs + 8 * e);
+    }
+    return;
+  }
+  const bool first = i < sg.ns;
+  // position of the key and its ring slot
+  const int ring = first ? 0 : ((p0 - sg.nw + (i - sg.ns)) - c.n_sink) % c.window;
+  if (!QUANT || first) {
+    const uint16_t* sk;
+    const uint16_t* sv;
+    if (!QUANT) {
+      const int slot = first ? i : c.n_sink + ring;
+      const size_t o = ((static_cast<size_t>(b) * (c.n_sink + c.window) + slot) * c.hkv + g) * D;
+      sk = static_cast<const uint16_t*>(c.k) + o;
+      sv = static_cast<const uint16_t*>(c.v) + o;
+    } else {
+      const size_t o = ((static_cast<size_t>(b) * c.n_sink + i) * c.hkv + g) * D;
+      sk = static_cast<const uint16_t*>(c.sink_k) + o;
+      sv = static_cast<const uint16_t*>(c.sink_v) + o;
+    }
+    for (int e = sub; e < nchunk8; e += 16) {
+      *reinterpret_cast<u32x4*>(kp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(sk + 8 * e);
+      *reinterpret_cast<u32x4*>(vp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(sv + 8 * e);
+    }
+    return;
+  }
+  // 8-bit ring row: code * scale in float32, rounded to bfloat16.
+  const size_t o = ((static_cast<size_t>(b) * c.window + ring) * c.hkv + g) * D;
+  const size_t si = (static_cast<size_t>(b) * c.hkv + g) * c.window + ring;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint8_t* codes = (which == 0 ? c.win_k : c.win_v) + o;
+    const float sc = (which == 0 ? c.win_k_scale : c.win_v_scale)[si];
+    uint16_t* out = (which == 0 ? kp : vp) + dst;
+    for (int e = sub; e < nchunk8; e += 16) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(codes + 8 * e);
+      u32x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = w[j >> 1];
+        const auto f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
+                               : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+        bf16x2 v2 = {static_cast<__bf16>(f[0] * sc), static_cast<__bf16>(f[1] * sc)};
+        r[j] = __builtin_bit_cast(uint32_t, v2);
+      }
+      *reinterpret_cast<u32x4*>(out + 8 * e) = r;
+    }
+  }
+}
+
+// 16 lanes per (sequence b, chunk row c, query head h): O, LSE and s of the
+// chunk rows from the packed forward's outputs.
+__global__ __launch_bounds__(256) void prefill_scatter_kernel(KvCache c, int chunk, int hq,
+                                                              const int32_t* __restrict__ n_seen, int lmax,
+                                                              const uint16_t* __restrict__ op,
+                                                              const float* __restrict__ lsep,
+                                                              const float* __restrict__ sp,
+                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                              float* __restrict__ s) {
+  const size_t unit = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (unit >= static_cast<size_t>(c.batch) * chunk * hq) return;
+  const int h = static_cast<int>(unit % hq);
+  const int cc = static_cast<int>((unit / hq) % chunk);
+  const int b = static_cast<int>(unit / (static_cast<size_t>(hq) * chunk));
+  const Seg sg = segment(c, n_seen[b], chunk);
+  const size_t src = (static_cast<size_t>(b) * lmax + (sg.L - chunk) + cc) * hq + h;
+  const size_t dst = unit;                            // (b * chunk + cc) * hq + h
+  const int D = c.d;
+  for (int e = sub; e < D / 8; e += 16)
+    *reinterpret_cast<u32x4*>(o + dst * D + 8 * e) = *reinterpret_cast<const u32x4*>(op + src * D + 8 * e);
+  if (sub == 0) {
+    lse[dst] = lsep[src];
+    if (s != nullptr) s[dst] = sp[src];
+  }
+}
 }  // namespace kvc
 
 hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void* v_new, int chunk,
@@ -102,6 +252,31 @@ hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(64), 0, st, c,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), chunk,
                      n_seen);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const void* k_new,
+                                         const void* v_new, int chunk, int hq, const int32_t* n_seen,
+                                         int lmax, void* kp, void* vp, void* qp, int32_t* cu,
+                                         int32_t* qstart, hipStream_t st) {
+  const size_t units = static_cast<size_t>(c.batch) * lmax * c.hkv;
+  if (units == 0) return hipSuccess;
+  auto kern = c.quantized ? kvc::prefill_gather_kernel<true> : kvc::prefill_gather_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((units + 15) / 16)), dim3(256), 0, st, c,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), chunk, hq, n_seen, lmax, static_cast<uint16_t*>(kp),
+                     static_cast<uint16_t*>(vp), static_cast<uint16_t*>(qp), cu, qstart);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvcache_prefill_scatter(const KvCache& c, int chunk, int hq, const int32_t* n_seen,
+                                          int lmax, const void* op, const float* lsep, const float* sp,
+                                          void* o, float* lse, float* s, hipStream_t st) {
+  const size_t units = static_cast<size_t>(c.batch) * chunk * hq;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(kvc::prefill_scatter_kernel, dim3(static_cast<unsigned>((units + 15) / 16)), dim3(256), 0,
+                     st, c, chunk, hq, n_seen, lmax, static_cast<const uint16_t*>(op), lsep, sp,
+                     static_cast<uint16_t*>(o), lse, s);
   return hipGetLastError();
 }
 

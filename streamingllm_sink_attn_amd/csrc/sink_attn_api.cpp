@@ -554,6 +554,124 @@ int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
   }
 }
 
+// Chunked prefill: workspace sections of the packed per-sequence samples.
+struct PrefillLayout {
+  size_t cu, qstart, kp, vp, qp, op, lsep, sp, total;
+  long long lmax;
+};
+
+PrefillLayout kvcache_prefill_layout(const sink_attn_kvcache_desc* c, int32_t chunk, int32_t hq) {
+  PrefillLayout l{};
+  l.lmax = static_cast<long long>(c->n_sink) + c->window + chunk;
+  const size_t rows = static_cast<size_t>(c->batch) * static_cast<size_t>(l.lmax);
+  const size_t D = static_cast<size_t>(c->head_dim);
+  size_t off = 0;
+  l.cu = off; off += round_up((2 * static_cast<size_t>(c->batch) + 1) * 4);
+  l.qstart = off; off += round_up(2 * static_cast<size_t>(c->batch) * 4);
+  l.kp = off; off += round_up(rows * c->num_kv_heads * D * 2);
+  l.vp = off; off += round_up(rows * c->num_kv_heads * D * 2);
+  l.qp = off; off += round_up(rows * hq * D * 2);
+  l.op = off; off += round_up(rows * hq * D * 2);
+  l.lsep = off; off += round_up(rows * hq * 4);
+  l.sp = off; off += round_up(rows * hq * 4);
+  l.total = off;
+  return l;
+}
+
+size_t sink_attn_kvcache_prefill_workspace_size(const sink_attn_kvcache_desc* cache, int32_t chunk,
+                                                int32_t num_q_heads) {
+  if (check_kvcache_desc(cache) != SINK_ATTN_OK || chunk < 0 || num_q_heads < 1) return 0;
+  if (static_cast<long long>(cache->batch) * chunk == 0) return 0;
+  return kvcache_prefill_layout(cache, chunk, num_q_heads).total;
+}
+
+int sink_attn_check_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q,
+                                    int32_t num_q_heads, const void* k_new, const void* v_new,
+                                    int32_t chunk, const int32_t* n_seen, float softmax_scale,
+                                    const void* o, const float* lse, const float* s,
+                                    size_t workspace_bytes) {
+  SA_TRY(check_kvcache_desc(cache));
+  if (chunk < 0) return fail(SINK_ATTN_INVALID_ARGUMENT, "chunk < 0");
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (num_q_heads > 65535) return fail(SINK_ATTN_UNSUPPORTED, "num_q_heads > 65535");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(SINK_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+  const long long lmax = static_cast<long long>(cache->n_sink) + cache->window + chunk;
+  const long long rows = static_cast<long long>(cache->batch) * lmax;
+  // packed rows, and the forward's grid (at most lmax/32 position tiles x
+  // 2*batch samples x num_q_heads head groups), within 32 bits
+  if (rows > 0x7fffffffLL || 2LL * cache->batch * ((lmax + 31) / 32) * num_q_heads > 0x7fffffffLL ||
+      static_cast<long long>(cache->batch) * chunk * num_q_heads > 0x7fffffffLL ||
+      rows * cache->num_kv_heads > 0x7fffffffLL)
+    return fail(SINK_ATTN_UNSUPPORTED, "batch x (n_sink + window + chunk) too large");
+  const bool need = static_cast<long long>(cache->batch) * chunk > 0;
+  SA_TRY(check_ptr(q, "q", 16, need));
+  SA_TRY(check_ptr(k_new, "k_new", 16, need));
+  SA_TRY(check_ptr(v_new, "v_new", 16, need));
+  SA_TRY(check_ptr(n_seen, "n_seen", 4, need));
+  SA_TRY(check_ptr(o, "o", 16, need));
+  SA_TRY(check_ptr(lse, "lse", 4, need));
+  SA_TRY(check_ptr(s, "s", 4, false));
+  const size_t ws = sink_attn_kvcache_prefill_workspace_size(cache, chunk, num_q_heads);
+  if (workspace_bytes < ws)
+    return fail(SINK_ATTN_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu", workspace_bytes, ws);
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q, int32_t num_q_heads,
+                              const void* k_new, const void* v_new, int32_t chunk,
+                              const int32_t* n_seen, float softmax_scale, const float* learnable_sink,
+                              void* o, float* lse, float* s, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  try {
+    SA_TRY(sink_attn_check_kvcache_prefill(cache, q, num_q_heads, k_new, v_new, chunk, n_seen,
+                                           softmax_scale, o, lse, s, workspace_bytes));
+    SA_TRY(check_ptr(learnable_sink, "learnable_sink", 4, false));
+    if (static_cast<long long>(cache->batch) * chunk == 0) return SINK_ATTN_OK;
+    SA_TRY(check_ptr(workspace, "workspace", 256, true));
+    const PrefillLayout l = kvcache_prefill_layout(cache, chunk, num_q_heads);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* cu = reinterpret_cast<int32_t*>(ws + l.cu);
+    int32_t* qstart = reinterpret_cast<int32_t*>(ws + l.qstart);
+    float* lsep = reinterpret_cast<float*>(ws + l.lsep);
+    float* sp = reinterpret_cast<float*>(ws + l.sp);
+    const sa::KvCache kc = to_kvcache(cache);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int lmax = static_cast<int>(l.lmax);
+    hipError_t e = sa::launch_kvcache_prefill_gather(kc, q, k_new, v_new, chunk, num_q_heads, n_seen, lmax,
+                                                     ws + l.kp, ws + l.vp, ws + l.qp, cu, qstart, st);
+    if (e == hipSuccess) {
+      sa::Prefill p;
+      p.cu = cu;
+      p.batch = 2 * cache->batch;
+      p.total = cache->batch * lmax;
+      p.max_seqlen = lmax;
+      p.hq = num_q_heads;
+      p.hkv = cache->num_kv_heads;
+      p.d = cache->head_dim;
+      p.dtype = SINK_ATTN_BF16;
+      p.scale = softmax_scale;
+      p.n_sink = cache->n_sink;
+      p.window = cache->window;
+      p.blocks = nullptr;
+      p.nqb = 0;
+      p.max_blocks = 0;
+      p.sink = learnable_sink;
+      p.qstart = qstart;
+      e = sa::fwd_mfma_supported(p)
+              ? sa::launch_fwd_mfma(p, ws + l.qp, ws + l.kp, ws + l.vp, ws + l.op, lsep, sp, nullptr, st)
+              : sa::launch_fwd_generic(p, ws + l.qp, ws + l.kp, ws + l.vp, ws + l.op, lsep, sp, nullptr, st);
+    }
+    if (e == hipSuccess)
+      e = sa::launch_kvcache_prefill_scatter(kc, chunk, num_q_heads, n_seen, lmax, ws + l.op, lsep, sp, o,
+                                             lse, s, st);
+    return hip_status(e, "sink_attn_kvcache_prefill launch");
+  } catch (...) {
+    return fail(SINK_ATTN_HIP_ERROR, "unexpected exception in sink_attn_kvcache_prefill");
+  }
+}
+
 int sink_attn_decode(const sink_attn_decode_desc* desc, const void* q, const void* k_cache,
                      const void* v_cache, void* o, float* lse, float* s, void* workspace,
                      size_t workspace_bytes, void* stream) {

@@ -277,6 +277,58 @@ def kvcache_q8_decode(batch: int = 128, n_sink: int = 4, window: int = 4092, hq:
                       1.0 / float(np.sqrt(d)))
 
 
+
+@dataclasses.dataclass
+class KvPrefill:
+    """A filled bf16 rolling cache (first tokens + a wrapped ring) and one
+    chunk of new tokens per stream, each stream at its own position."""
+    batch: int
+    n_sink: int
+    window: int
+    chunk: int
+    hq: int
+    hkv: int
+    d: int
+    k_cache: np.ndarray      # float32 (bf16-exact) [B, n_sink + window, Hkv, D]
+    v_cache: np.ndarray
+    q: np.ndarray            # float32 (bf16-exact) [B, chunk, Hq, D]
+    k_new: np.ndarray        # float32 (bf16-exact) [B, chunk, Hkv, D]
+    v_new: np.ndarray
+    n_seen: np.ndarray       # int32 [B]: tokens cached before the chunk (>= n_sink + window)
+    sink: np.ndarray         # float32 [Hq]
+    scale: float
+
+    def valid_pairs(self) -> int:
+        """(query row, key) pairs the StreamingLLM mask keeps, over all heads."""
+        total = 0
+        for p0 in self.n_seen:
+            p = int(p0) + np.arange(self.chunk)
+            lo = np.maximum(p - self.window + 1, 0)              # window keys [lo, p]
+            win = p - lo + 1
+            first = np.minimum(self.n_sink, lo)                  # first tokens below the window
+            total += int(np.sum(win + first))
+        return total * self.hq
+
+
+def kvcache_prefill(batch: int = 8, n_sink: int = 4, window: int = 1024, chunk: int = 1024, hq: int = 32,
+                    hkv: int = 8, d: int = 128, seed: int = 0) -> KvPrefill:
+    """Streams of the StreamingLLM prefill shape (4 first tokens, a
+    1024-token window, Hq=32, Hkv=8, D=128) taking their next 1024-token
+    chunk at positions past the first window."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    slots = n_sink + window
+    kc = _draw(rng, (batch, slots, hkv, d), "bf16").f32
+    vc = _draw(rng, (batch, slots, hkv, d), "bf16").f32
+    q = _draw(rng, (batch, chunk, hq, d), "bf16").f32
+    kn = _draw(rng, (batch, chunk, hkv, d), "bf16", 0.5).f32
+    vn = _draw(rng, (batch, chunk, hkv, d), "bf16").f32
+    kc[:, n_sink:] *= np.float32(0.5)                             # K scaled as in the prefill workloads
+    kc[:, :n_sink] *= np.float32(0.5)
+    n_seen = rng.integers(slots, 8 * slots, size=batch).astype(np.int32)
+    a = rng.standard_normal(size=hq, dtype=np.float32)
+    return KvPrefill(batch, n_sink, window, chunk, hq, hkv, d, kc, vc, q, kn, vn, n_seen, a,
+                     1.0 / float(np.sqrt(d)))
+
 # ---------------------------------------------------------------------------
 # The five named workloads
 # ---------------------------------------------------------------------------

@@ -223,3 +223,32 @@ def test_check_kvcache_append_and_decode():
         assert dec(_kdesc(**q8), splits=4, ws=need - 1) == B.WORKSPACE_TOO_SMALL
     # one split on the 8-bit ring: no partials, no workspace
     assert L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(_kdesc(**_Q8)), 8, 1) == 0
+
+
+def test_check_kvcache_prefill():
+    L = B.lib()
+
+    def pre(desc, hq=8, chunk=16, q=FAKE, k=FAKE, v=FAKE, n=FAKE, scale=0.1, o=FAKE, lse=FAKE, s=None,
+            ws=None):
+        if ws is None:
+            ws = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(desc), chunk, hq)
+        return L.sink_attn_check_kvcache_prefill(ctypes.byref(desc), q, hq, k, v, chunk, n, scale, o, lse,
+                                                 s, ws)
+    assert pre(_kdesc()) == B.OK and pre(_kdesc(**_Q8)) == B.OK
+    assert pre(_kdesc(), chunk=0, q=None, k=None, v=None, n=None, o=None, lse=None) == B.OK
+    assert L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(_kdesc()), 0, 8) == 0
+    assert pre(_kdesc(), chunk=-1) == B.INVALID_ARGUMENT
+    assert pre(_kdesc(), hq=5) == B.INVALID_ARGUMENT                        # not a multiple of Hkv
+    assert pre(_kdesc(), scale=float("nan")) == B.INVALID_ARGUMENT
+    for name in ("q", "k", "v", "n", "o", "lse"):
+        assert pre(_kdesc(), **{name: None}) == B.INVALID_ARGUMENT, name
+    assert pre(_kdesc(), q=FAKE + 4) == B.INVALID_ARGUMENT                  # misaligned
+    assert pre(_kdesc(), s=FAKE) == B.OK
+    assert pre(_kdesc(head_dim=64, **_Q8)) == B.UNSUPPORTED
+    d = _kdesc()
+    need = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(d), 16, 8)
+    rows = d.batch * (d.n_sink + d.window + 16)
+    # packed K, V (Hkv heads), Q, O (Hq heads) in bf16, LSE and s in float32
+    assert need >= rows * (2 * d.num_kv_heads * d.head_dim * 2 + 2 * 8 * d.head_dim * 2 + 2 * 8 * 4)
+    assert pre(d, ws=need - 1) == B.WORKSPACE_TOO_SMALL
+    assert pre(_kdesc(batch=60000, window=1 << 20)) == B.UNSUPPORTED         # packed rows past 2^31

@@ -157,3 +157,81 @@ def test_decode_q8_fullsize_sampled():
         assert err.max() <= TOL_BF16["o_max"], f"seq {b}: O max err {err.max():.3e}"
         assert_lse(hl[b], rl[0], TOL_BF16["lse"])
         assert np.max(np.abs(hs[b] - rs[0])) <= TOL_BF16["s"]
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill against the cache
+# ---------------------------------------------------------------------------
+
+def _check_prefill_rows(got, want, rows=None):
+    o, lse, s = (host(x.float()) if x.dtype == torch.bfloat16 else host(x) for x in got)
+    ro, rl, rs = want
+    if rows is not None:
+        idx = tuple(np.array(rows).T)
+        o, lse, s, ro, rl, rs = o[idx], lse[idx], s[idx], ro[idx], rl[idx], rs[idx]
+    err = np.abs(o - ro)
+    assert err.max() <= TOL_BF16["o_max"], f"O max err {err.max():.3e}"
+    assert err.mean() <= TOL_BF16["o_mean"]
+    assert_lse(lse, rl, TOL_BF16["lse"])
+    assert np.max(np.abs(s - rs)) <= TOL_BF16["s"]
+
+
+def _prefill_stream(rng, B, hq, hkv, d, n_sink, window, quantized, chunks, start=None, sink=True):
+    """Each chunk: prefill against the cache (GPU and oracle, compared), then
+    append it to both caches."""
+    cache = sa.KvCache(B, n_sink, window, hkv, d, quantized)
+    ref = KO.new_cache(B, n_sink, window, hkv, d, quantized)
+    seen = np.zeros(B, np.int32) if start is None else np.array(start, np.int32)
+    a = rng.standard_normal(hq).astype(np.float32) if sink else None
+    at = torch.from_numpy(a).to(DEV) if sink else None
+    for c in chunks:
+        q, qt = _bf16(rng, (B, c, hq, d))
+        k, kt = _bf16(rng, (B, c, hkv, d), 0.7)
+        v, vt = _bf16(rng, (B, c, hkv, d))
+        st = torch.from_numpy(seen).to(DEV)
+        got = sa.kvcache_prefill(cache, qt, kt, vt, st, 0.09, at)
+        torch.cuda.synchronize()
+        _check_prefill_rows(got, KO.cache_prefill(q, ref, k, v, seen, n_sink, window, 0.09, sink=a))
+        sa.kvcache_append(cache, kt, vt, st)
+        KO.append(ref, k, v, seen, n_sink, window)
+        seen = seen + c
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+@pytest.mark.parametrize("n_sink,window,chunks,start", [(4, 40, [1, 7, 33, 2, 90, 1], [0, 3, 50]),
+                                                        (0, 32, [5, 64], None),
+                                                        (6, 17, [3, 3, 40], [0, 0, 9])])
+def test_prefill_over_cache(quantized, n_sink, window, chunks, start):
+    print(f"[case] kvcache prefill q={quantized} {n_sink} {window} {chunks} {start}", flush=True)
+    rng = np.random.default_rng(21)
+    _prefill_stream(rng, 3, 8, 2, 128, n_sink, window, quantized, chunks, start)
+
+
+def test_prefill_over_cache_d64_and_no_sink():
+    """bf16 layout with D = 64 (the generic forward) and without a sink."""
+    print("[case] kvcache prefill d64 / no sink", flush=True)
+    rng = np.random.default_rng(22)
+    _prefill_stream(rng, 2, 4, 1, 64, 4, 20, False, [5, 30, 2], start=[0, 11])
+    _prefill_stream(rng, 2, 8, 2, 128, 4, 20, False, [9, 30], sink=False)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_fullsize_sampled():
+    """8 streams x 1024-token chunks against (4 + 1024)-slot caches, Hq=32,
+    Hkv=8: the bench workload, checked on sampled rows."""
+    print("[case] kvcache prefill fullsize", flush=True)
+    wl = W.kvcache_prefill()
+    cache = sa.KvCache(wl.batch, wl.n_sink, wl.window, wl.hkv, wl.d, quantized=False)
+    cache.k.copy_(torch.from_numpy(wl.k_cache).to(torch.bfloat16))
+    cache.v.copy_(torch.from_numpy(wl.v_cache).to(torch.bfloat16))
+    dev_ = lambda x: torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+    got = sa.kvcache_prefill(cache, dev_(wl.q), dev_(wl.k_new), dev_(wl.v_new),
+                             torch.from_numpy(wl.n_seen).to(DEV), wl.scale, torch.from_numpy(wl.sink).to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(23)
+    rows = [(int(b), int(c)) for b, c in zip(rng.integers(0, wl.batch, 10), rng.integers(0, wl.chunk, 10))]
+    rows += [(0, 0), (wl.batch - 1, wl.chunk - 1), (3, 63), (3, 64)]
+    ref = dict(quantized=False, k=wl.k_cache, v=wl.v_cache)
+    want = KO.cache_prefill(wl.q, ref, wl.k_new, wl.v_new, wl.n_seen, wl.n_sink, wl.window, wl.scale,
+                            sink=wl.sink, rows=rows)
+    _check_prefill_rows(got, want, rows)
