@@ -89,8 +89,10 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   const int L = p.cu[wc.b + 1] - t0;
   const int p0 = wc.pt * geo.P;
   if (p0 >= L) return;                               // uniform over the workgroup
-  if (p.qstart != nullptr && p0 + geo.P <= p.qstart[wc.b]) return;
   const int p1 = min(L, p0 + geo.P);
+  const int qs = p.qstart != nullptr ? p.qstart[wc.b] : 0;   // rows before qs: not needed
+  if (p1 <= qs) return;
+  const int tq = p.qo_base != nullptr ? p.qo_base[wc.b] : t0;   // row of local 0 in Q, O, LSE, s
 
   const int tid = threadIdx.x;
   // wavefront index as a scalar, so per-wavefront tile decisions are
@@ -110,8 +112,8 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   // Q^T as the B operand: lane (query l32, half gq) holds dims gq*64 + ks*8
   // .. +8 for k-step ks (the K fragments use the same order).
   bf16x8 qf[8];
-  if (qi < L) {
-    const uint16_t* src = Q + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + gq * 64;
+  if (qi < L && qi >= qs) {
+    const uint16_t* src = Q + (static_cast<size_t>(tq + qi) * p.hq + h) * D + gq * 64;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + ks * 8));
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   // Epilogue: L_orig = alpha*m + ln l; s = sigma(L_orig - a_h); O = acc * s / l.
   const float lt = xhalf_sum(lsum);
   const float l0t = GATE ? xhalf_sum(l0) : 0.f;
-  if (qi >= wq1) return;
+  if (qi >= wq1 || qi < qs) return;
   const bool has_sink = p.sink != nullptr;
   float L_orig, s_val, mul;
   if (lt > 0.f) {
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     s_val = has_sink ? 0.f : 1.f;
     mul = 0.f;
   }
-  uint16_t* dst = O + (static_cast<size_t>(t0 + qi) * p.hq + h) * D + 4 * gq;
+  uint16_t* dst = O + (static_cast<size_t>(tq + qi) * p.hq + h) * D + 4 * gq;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
       *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * u) = pk;
     }
   if (gq == 0) {
-    const size_t r = static_cast<size_t>(t0 + qi) * p.hq + h;
+    const size_t r = static_cast<size_t>(tq + qi) * p.hq + h;
     lse_out[r] = L_orig;
     if (s_out) s_out[r] = s_val;
     if constexpr (GATE) gate_out[r] = lt > 0.f ? (lt - l0t) / lt : 0.f;

@@ -24,6 +24,9 @@ struct Prefill {
   // [batch] or nullptr: rows before qstart[b] of sample b are not needed
   // (a workgroup whose rows all lie before it exits; the forward only).
   const int32_t* qstart = nullptr;
+  // [batch] or nullptr: the Q, O, LSE and s rows of sample b start at row
+  // qo_base[b] instead of cu[b] (K and V stay at cu[b]); the forward only.
+  const int32_t* qo_base = nullptr;
 };
 
 // Backward workspace carve-up (float32 unless noted).
@@ -106,12 +109,13 @@ hipError_t launch_visit_map(const Prefill& p, uint8_t* out, hipStream_t st);
 // Append `chunk` tokens per sequence (k_new, v_new bf16 [B, chunk, Hkv, D],
 // stream positions n_seen[b] + c) into the cache.
 // Chunked prefill against the cache: the packed per-sequence samples (K, V,
-// Q rows; cu of 2*batch + 1 entries, qstart of 2*batch) and the copy of the
-// chunk rows' outputs back to [batch, chunk, ...] order.
+// and Q rows when qp is set; cu of 2*batch + 1 entries, qstart and qo_base of
+// 2*batch) and the copy of the chunk rows' outputs back to [batch, chunk, ...]
+// order (for the generic forward, which reads and writes packed rows).
 hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const void* k_new,
                                          const void* v_new, int chunk, int hq, const int32_t* n_seen,
                                          int lmax, void* kp, void* vp, void* qp, int32_t* cu,
-                                         int32_t* qstart, hipStream_t st);
+                                         int32_t* qstart, int32_t* qo_base, hipStream_t st);
 hipError_t launch_kvcache_prefill_scatter(const KvCache& c, int chunk, int hq, const int32_t* n_seen,
                                           int lmax, const void* op, const float* lsep, const float* sp,
                                           void* o, float* lse, float* s, hipStream_t st);

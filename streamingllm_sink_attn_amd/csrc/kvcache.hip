@@ -122,8 +122,10 @@ __device__ __forceinline__ Seg segment(const KvCache& c, int p0, int chunk) {
 }
 
 // 16 lanes per (sequence b, segment row i, KV head g): the K and V row of the
-// key at row i (cache or chunk) and, for chunk rows, the G query rows.
-// Also writes the samples' bounds (cu: 2B + 1, qstart: 2B).
+// key at row i (cache or chunk) and, for chunk rows with qp set, the G query
+// rows.  Also writes the samples' bounds (cu: 2B + 1, qstart: 2B) and, when
+// qo_base is set, where each sample's rows sit in the caller's [B, chunk]
+// Q and outputs (the forward then reads and writes those directly).
 template <bool QUANT>
 __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k_new,
@@ -132,7 +134,8 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const ui
                                                              int lmax, uint16_t* __restrict__ kp,
                                                              uint16_t* __restrict__ vp,
                                                              uint16_t* __restrict__ qp, int32_t* __restrict__ cu,
-                                                             int32_t* __restrict__ qstart) {
+                                                             int32_t* __restrict__ qstart,
+                                                             int32_t* __restrict__ qo_base) {
   const size_t unit = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const size_t units = static_cast<size_t>(c.batch) * lmax * c.hkv;
@@ -148,6 +151,10 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const ui
     cu[2 * b + 1] = b * lmax + sg.L;
     qstart[2 * b] = sg.L - chunk;
     qstart[2 * b + 1] = lmax - sg.L;
+    if (qo_base != nullptr) {                         // chunk row cc read and written at b*chunk + cc
+      qo_base[2 * b] = b * chunk - (sg.L - chunk);
+      qo_base[2 * b + 1] = 0;
+    }
     if (b == c.batch - 1) cu[2 * c.batch] = c.batch * lmax;
   }
   if (i >= sg.L) return;
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const ui
       *reinterpret_cast<u32x4*>(kp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
       *reinterpret_cast<u32x4*>(vp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
     }
-    const int G = hq / c.hkv;
+    const int G = qp != nullptr ? hq / c.hkv : 0;    // Q rows only for a packed copy
     for (int hh = 0; hh < G; ++hh) {
       const int h = g * G + hh;
       const size_t qs = ((static_cast<size_t>(b) * chunk + cc) * hq + h) * D;
@@ -258,14 +265,14 @@ hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void
 hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const void* k_new,
                                          const void* v_new, int chunk, int hq, const int32_t* n_seen,
                                          int lmax, void* kp, void* vp, void* qp, int32_t* cu,
-                                         int32_t* qstart, hipStream_t st) {
+                                         int32_t* qstart, int32_t* qo_base, hipStream_t st) {
   const size_t units = static_cast<size_t>(c.batch) * lmax * c.hkv;
   if (units == 0) return hipSuccess;
   auto kern = c.quantized ? kvc::prefill_gather_kernel<true> : kvc::prefill_gather_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((units + 15) / 16)), dim3(256), 0, st, c,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), chunk, hq, n_seen, lmax, static_cast<uint16_t*>(kp),
-                     static_cast<uint16_t*>(vp), static_cast<uint16_t*>(qp), cu, qstart);
+                     static_cast<uint16_t*>(vp), static_cast<uint16_t*>(qp), cu, qstart, qo_base);
   return hipGetLastError();
 }
 

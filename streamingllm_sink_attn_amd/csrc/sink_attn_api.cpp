@@ -555,25 +555,32 @@ int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
 }
 
 // Chunked prefill: workspace sections of the packed per-sequence samples.
+// With head_dim 128 the matrix-core forward reads Q and writes the outputs in
+// the caller's [B, chunk] layout (direct); otherwise the generic forward works
+// on packed Q / O copies.
 struct PrefillLayout {
-  size_t cu, qstart, kp, vp, qp, op, lsep, sp, total;
+  size_t cu, qstart, qo_base, kp, vp, qp, op, lsep, sp, total;
   long long lmax;
+  bool direct;
 };
 
 PrefillLayout kvcache_prefill_layout(const sink_attn_kvcache_desc* c, int32_t chunk, int32_t hq) {
   PrefillLayout l{};
   l.lmax = static_cast<long long>(c->n_sink) + c->window + chunk;
+  l.direct = c->head_dim == 128;
   const size_t rows = static_cast<size_t>(c->batch) * static_cast<size_t>(l.lmax);
   const size_t D = static_cast<size_t>(c->head_dim);
+  const size_t qrows = l.direct ? 0 : rows;
   size_t off = 0;
   l.cu = off; off += round_up((2 * static_cast<size_t>(c->batch) + 1) * 4);
   l.qstart = off; off += round_up(2 * static_cast<size_t>(c->batch) * 4);
+  l.qo_base = off; off += round_up(2 * static_cast<size_t>(c->batch) * 4);
   l.kp = off; off += round_up(rows * c->num_kv_heads * D * 2);
   l.vp = off; off += round_up(rows * c->num_kv_heads * D * 2);
-  l.qp = off; off += round_up(rows * hq * D * 2);
-  l.op = off; off += round_up(rows * hq * D * 2);
-  l.lsep = off; off += round_up(rows * hq * 4);
-  l.sp = off; off += round_up(rows * hq * 4);
+  l.qp = off; off += round_up(qrows * hq * D * 2);
+  l.op = off; off += round_up(qrows * hq * D * 2);
+  l.lsep = off; off += round_up(qrows * hq * 4);
+  l.sp = off; off += round_up(qrows * hq * 4);
   l.total = off;
   return l;
 }
@@ -639,8 +646,10 @@ int sink_attn_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q
     const sa::KvCache kc = to_kvcache(cache);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lmax = static_cast<int>(l.lmax);
+    int32_t* qo_base = l.direct ? reinterpret_cast<int32_t*>(ws + l.qo_base) : nullptr;
     hipError_t e = sa::launch_kvcache_prefill_gather(kc, q, k_new, v_new, chunk, num_q_heads, n_seen, lmax,
-                                                     ws + l.kp, ws + l.vp, ws + l.qp, cu, qstart, st);
+                                                     ws + l.kp, ws + l.vp, l.direct ? nullptr : ws + l.qp,
+                                                     cu, qstart, qo_base, st);
     if (e == hipSuccess) {
       sa::Prefill p;
       p.cu = cu;
@@ -659,11 +668,13 @@ int sink_attn_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q
       p.max_blocks = 0;
       p.sink = learnable_sink;
       p.qstart = qstart;
-      e = sa::fwd_mfma_supported(p)
-              ? sa::launch_fwd_mfma(p, ws + l.qp, ws + l.kp, ws + l.vp, ws + l.op, lsep, sp, nullptr, st)
-              : sa::launch_fwd_generic(p, ws + l.qp, ws + l.kp, ws + l.vp, ws + l.op, lsep, sp, nullptr, st);
+      p.qo_base = qo_base;
+      if (l.direct != sa::fwd_mfma_supported(p))
+        return fail(SINK_ATTN_HIP_ERROR, "internal: chunked prefill path mismatch");
+      e = l.direct ? sa::launch_fwd_mfma(p, q, ws + l.kp, ws + l.vp, o, lse, s, nullptr, st)
+                   : sa::launch_fwd_generic(p, ws + l.qp, ws + l.kp, ws + l.vp, ws + l.op, lsep, sp, nullptr, st);
     }
-    if (e == hipSuccess)
+    if (e == hipSuccess && !l.direct)
       e = sa::launch_kvcache_prefill_scatter(kc, chunk, num_q_heads, n_seen, lmax, ws + l.op, lsep, sp, o,
                                              lse, s, st);
     return hip_status(e, "sink_attn_kvcache_prefill launch");

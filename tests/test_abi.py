@@ -245,10 +245,14 @@ def test_check_kvcache_prefill():
     assert pre(_kdesc(), q=FAKE + 4) == B.INVALID_ARGUMENT                  # misaligned
     assert pre(_kdesc(), s=FAKE) == B.OK
     assert pre(_kdesc(head_dim=64, **_Q8)) == B.UNSUPPORTED
-    d = _kdesc()
-    need = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(d), 16, 8)
-    rows = d.batch * (d.n_sink + d.window + 16)
-    # packed K, V (Hkv heads), Q, O (Hq heads) in bf16, LSE and s in float32
-    assert need >= rows * (2 * d.num_kv_heads * d.head_dim * 2 + 2 * 8 * d.head_dim * 2 + 2 * 8 * 4)
-    assert pre(d, ws=need - 1) == B.WORKSPACE_TOO_SMALL
+    for hd in (128, 64):
+        d = _kdesc(head_dim=hd)
+        need = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(d), 16, 8)
+        rows = d.batch * (d.n_sink + d.window + 16)
+        # packed K, V (Hkv heads) in bf16; head_dim 128 reads Q and writes the
+        # outputs in place, other sizes also pack Q, O (bf16) and LSE, s (float32)
+        kv = 2 * d.num_kv_heads * hd * 2
+        qo = 0 if hd == 128 else 2 * 8 * hd * 2 + 2 * 8 * 4
+        assert rows * (kv + qo) <= need <= rows * (kv + qo) + 16 * 256
+        assert pre(d, ws=need - 1) == B.WORKSPACE_TOO_SMALL
     assert pre(_kdesc(batch=60000, window=1 << 20)) == B.UNSUPPORTED         # packed rows past 2^31
