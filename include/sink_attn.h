@@ -200,8 +200,9 @@ typedef struct sink_attn_kvcache_desc {
 /*
  * Append a chunk of new tokens to every sequence's cache.
  *   k_new, v_new  bfloat16 [B, chunk, Hkv, D]: the new tokens in stream order.
- *   n_seen        device int32 [B]: tokens each stream held before this call;
- *                 token c of sequence b has stream position n_seen[b] + c.
+ *   n_seen        device int32 [B] (>= 0, n_seen[b] + chunk < 2^31): tokens
+ *                 each stream held before this call; token c of sequence b
+ *                 has stream position n_seen[b] + c.
  * Each token is written to its slot (quantized ring rows with their scales),
  * overwriting the token that slot held; a chunk token that a later token of
  * the same chunk would overwrite at once is not written, so no slot has two
@@ -242,7 +243,8 @@ int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
  * 8-bit ring enters as code * scale rounded to bfloat16.
  *   q             bfloat16 [B, chunk, num_q_heads, D].
  *   k_new, v_new  bfloat16 [B, chunk, Hkv, D]: the chunk's keys and values.
- *   n_seen        device int32 [B] (>= 0): tokens the cache has taken so far.
+ *   n_seen        device int32 [B] (>= 0, n_seen[b] + chunk < 2^31): tokens
+ *                 the cache has taken so far (a negative count reads as 0).
  *   o             output bfloat16 [B, chunk, num_q_heads, D]; lse, s float32
  *                 [B, chunk, num_q_heads] as sink_attn_fwd (s may be NULL).
  *   workspace     sink_attn_kvcache_prefill_workspace_size bytes, 256-byte

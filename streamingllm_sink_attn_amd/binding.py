@@ -342,13 +342,30 @@ class KvCache:
                            win_k_scale=ptr(self.win_k_scale), win_v_scale=ptr(self.win_v_scale))
 
 
+def _expect(t, shape, dtype, name):
+    """The C ABI sees pointers only: shapes and dtypes are checked here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise SinkAttnError(INVALID_ARGUMENT, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise SinkAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _heads(q, cache: KvCache, axis):
+    hq = int(q.shape[axis]) if q.dim() > axis else 0
+    if hq < 1 or hq % cache.hkv != 0:
+        raise SinkAttnError(INVALID_ARGUMENT, "query heads must be a positive multiple of the cache's KV heads")
+    return hq
+
+
 def kvcache_append(cache: KvCache, k_new, v_new, n_seen, stream=None):
     """Append k_new, v_new (bf16 [B, C, Hkv, D]) at stream positions n_seen[b] + c."""
     _need_cuda(k_new, v_new, n_seen)
-    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
-        raise SinkAttnError(UNSUPPORTED, "the cache takes bfloat16 tokens")
-    if n_seen.dtype != torch.int32:
-        raise SinkAttnError(INVALID_ARGUMENT, "n_seen must be int32")
+    C = int(k_new.shape[1]) if k_new.dim() == 4 else -1
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _expect(t, (cache.batch, C, cache.hkv, cache.d), torch.bfloat16, name)
+    _expect(n_seen, (cache.batch,), torch.int32, "n_seen")
     desc = cache.desc()
     _check(lib().sink_attn_kvcache_append(ctypes.byref(desc), _p(k_new), _p(v_new),
                                           int(k_new.shape[1]), _p(n_seen), _stream(stream)))
@@ -358,11 +375,14 @@ def kvcache_decode(cache: KvCache, q, n_tokens, softmax_scale=None, learnable_si
                    num_splits=0, return_s=True, out=None, stream=None):
     """Decode one query per sequence over the cache (n_tokens[b] tokens appended,
     the current one included).  Returns (o, lse, s or None)."""
-    _need_cuda(q, n_tokens, learnable_sink)
-    if n_tokens.dtype != torch.int32:
-        raise SinkAttnError(INVALID_ARGUMENT, "n_tokens must be int32")
+    _need_cuda(q, n_tokens, learnable_sink, out)
+    hq = _heads(q, cache, 1)
+    B = cache.batch
+    _expect(q, (B, hq, cache.d), torch.bfloat16, "q")
+    _expect(n_tokens, (B,), torch.int32, "n_tokens")
+    _expect(learnable_sink, (hq,), torch.float32, "learnable_sink")
+    _expect(out, (B, hq, cache.d), torch.bfloat16, "out")
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    B, hq, _ = q.shape
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
     s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
@@ -383,11 +403,16 @@ def kvcache_prefill(cache: KvCache, q, k_new, v_new, n_seen, softmax_scale=None,
     before this chunk) and the chunk itself.  The cache is not written: call
     kvcache_append(cache, k_new, v_new, n_seen) afterwards.  Returns (o [B, C,
     Hq, D], lse [B, C, Hq], s or None)."""
-    _need_cuda(q, k_new, v_new, n_seen, learnable_sink)
-    if n_seen.dtype != torch.int32:
-        raise SinkAttnError(INVALID_ARGUMENT, "n_seen must be int32")
+    _need_cuda(q, k_new, v_new, n_seen, learnable_sink, out)
+    hq = _heads(q, cache, 2)
+    B, C = cache.batch, int(q.shape[1])
+    _expect(q, (B, C, hq, cache.d), torch.bfloat16, "q")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _expect(t, (B, C, cache.hkv, cache.d), torch.bfloat16, name)
+    _expect(n_seen, (B,), torch.int32, "n_seen")
+    _expect(learnable_sink, (hq,), torch.float32, "learnable_sink")
+    _expect(out, (B, C, hq, cache.d), torch.bfloat16, "out")
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    B, C, hq, _ = q.shape
     o = out if out is not None else torch.empty_like(q)
     lse = torch.empty((B, C, hq), dtype=torch.float32, device=q.device)
     s = torch.empty((B, C, hq), dtype=torch.float32, device=q.device) if return_s else None

@@ -256,3 +256,21 @@ def test_check_kvcache_prefill():
         assert rows * (kv + qo) <= need <= rows * (kv + qo) + 16 * 256
         assert pre(d, ws=need - 1) == B.WORKSPACE_TOO_SMALL
     assert pre(_kdesc(batch=60000, window=1 << 20)) == B.UNSUPPORTED         # packed rows past 2^31
+
+
+def test_binding_cache_shape_checks():
+    """The C ABI sees only pointers: the binding checks cache-call shapes."""
+    import torch
+
+    class _C:
+        batch, hkv, d = 2, 2, 128
+    t = torch.zeros((2, 5, 2, 128), dtype=torch.bfloat16)
+    B._expect(t, (2, 5, 2, 128), torch.bfloat16, "k_new")
+    B._expect(None, (1,), torch.int32, "unused")
+    for shape, dtype in (((2, 5, 1, 128), torch.bfloat16), ((2, 5, 2, 128), torch.float32)):
+        with pytest.raises(B.SinkAttnError):
+            B._expect(t, shape, dtype, "k_new")
+    assert B._heads(torch.zeros((2, 5, 8, 128)), _C, 2) == 8
+    for hq in (0, 3):
+        with pytest.raises(B.SinkAttnError):
+            B._heads(torch.zeros((2, 5, hq, 128)), _C, 2)
