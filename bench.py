@@ -317,8 +317,25 @@ def bench_kvcache_prefill(torch, sa, W, steps, warmup):
 
     ms, _ = Timer(torch).run(step, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
+    # the same call against the 8-bit cache (ring rows dequantised on the way
+    # in): random codes and row scales of unit-normal size, the bf16 first tokens
+    qc = sa.KvCache(wl.batch, wl.n_sink, wl.window, wl.hkv, wl.d, quantized=True)
+    qc.sink_k.copy_(cache.k[:, :wl.n_sink])
+    qc.sink_v.copy_(cache.v[:, :wl.n_sink])
+    g = torch.Generator(device="cpu").manual_seed(1)
+    for t in (qc.win_k, qc.win_v):
+        t.copy_(torch.randint(0, 0x7F, tuple(t.shape), generator=g, dtype=torch.uint8)
+                | (torch.randint(0, 2, tuple(t.shape), generator=g, dtype=torch.uint8) << 7))
+    for t in (qc.win_k_scale, qc.win_v_scale):
+        t.copy_(torch.rand(tuple(t.shape), generator=g) * (2.0 / 448) + 2.0 / 448)
+
+    def step_q8():
+        sa.kvcache_prefill(qc, q, kn, vn, seen, wl.scale, sink, out=o)
+
+    ms8, _ = Timer(torch).run(step_q8, steps, warmup)
     return {"workload": "streaming_chunked_prefill", "unit": "TFLOP/s", "value": round(tf, 2),
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_step": round(ms, 4),
+            "q8_cache": {"ms": round(ms8, 4), "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2)},
             "valid_pairs": pairs,
             "config": {"batch": wl.batch, "chunk": wl.chunk, "n_sink": wl.n_sink, "window": wl.window,
                        "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "cache": "bf16"}}
