@@ -103,6 +103,19 @@ def test_decode_over_cache(quantized, splits):
 
 
 @pytest.mark.parametrize("quantized", [False, True])
+def test_decode_over_cache_odd_window_and_groups(quantized):
+    """A ring length that is not a multiple of 4 (the 8-bit decode then reads
+    scales one slot at a time), 5 first tokens, and 3 query heads per KV head."""
+    print(f"[case] kvcache decode odd window q={quantized}", flush=True)
+    rng = np.random.default_rng(15)
+    n_sink, window = 5, 301
+    for chunks in ([4], [9, 100], [9, 100, 400]):
+        cache, ref, seen = _stream(rng, 3, 2, 128, n_sink, window, quantized, chunks)
+        for splits in (0, 2):
+            _check_decode(cache, ref, seen, n_sink, window, 6, splits, rng)
+
+
+@pytest.mark.parametrize("quantized", [False, True])
 def test_decode_ignores_unwritten_slots(quantized):
     """Ring slots not yet written may hold anything: NaN codes, values and
     scales there change nothing."""
@@ -205,6 +218,15 @@ def test_prefill_over_cache(quantized, n_sink, window, chunks, start):
     print(f"[case] kvcache prefill q={quantized} {n_sink} {window} {chunks} {start}", flush=True)
     rng = np.random.default_rng(21)
     _prefill_stream(rng, 3, 8, 2, 128, n_sink, window, quantized, chunks, start)
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+def test_prefill_over_cache_three_heads_per_group(quantized):
+    """3 query heads per KV head (one head per workgroup, 256-row position
+    tiles) and an odd window."""
+    print(f"[case] kvcache prefill G=3 q={quantized}", flush=True)
+    rng = np.random.default_rng(24)
+    _prefill_stream(rng, 2, 6, 2, 128, 5, 301, quantized, [7, 300, 260], start=[0, 40])
 
 
 def test_prefill_over_cache_d64_and_no_sink():
