@@ -68,3 +68,55 @@ def test_graph_replays_match_eager(name):
                     f"replay {r}: {nm} differs"
             else:
                 assert torch.equal(g, e), f"replay {r}: {nm} differs"
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+def test_graph_cache_step_replays_match_eager(quantized):
+    """A serving step on the rolling cache captured as one graph: restore the
+    cache from a snapshot, chunked prefill, append the chunk, decode with two
+    splits.  Every replay, with eager work between, matches the eager step bit
+    for bit (outputs and the cache after the append)."""
+    print(f"[case] graph cache step q={quantized}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(13)
+    B, hq, hkv, d, n_sink, window, C = 3, 8, 2, 128, 4, 120, 48
+    rnd = lambda *shape, s=1.0: (torch.randn(*shape, generator=g) * s).to(torch.bfloat16).to(DEV)
+    cache = sa.KvCache(B, n_sink, window, hkv, d, quantized)
+    seen0 = torch.tensor([0, 30, 200], dtype=torch.int32, device=DEV)
+    sa.kvcache_append(cache, rnd(B, 200, hkv, d), rnd(B, 200, hkv, d), torch.zeros_like(seen0))
+    seen = seen0                                    # positions of the chunk's first token
+    state = [t for t in (cache.k, cache.v, cache.sink_k, cache.sink_v, cache.win_k, cache.win_v,
+                         cache.win_k_scale, cache.win_v_scale) if t is not None]
+    snap = [t.clone() for t in state]
+    q, kn, vn = rnd(B, C, hq, d), rnd(B, C, hkv, d, s=0.7), rnd(B, C, hkv, d)
+    q1 = rnd(B, hq, d)
+    n_tokens = seen + C
+    sink = torch.randn(hq, generator=g).to(DEV)
+
+    def step():
+        for t, s0 in zip(state, snap):
+            t.copy_(s0)
+        o, lse, s = sa.kvcache_prefill(cache, q, kn, vn, seen, 0.09, sink)
+        sa.kvcache_append(cache, kn, vn, seen)
+        od, ld, sd = sa.kvcache_decode(cache, q1, n_tokens, 0.09, sink, num_splits=2)
+        return [o, lse, s, od, ld, sd] + state
+
+    eager = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for r in range(3):
+        junk = torch.randn(1 << 16, device=DEV)
+        junk.mul_(2.0).sum().item()
+        for t in state:                              # disturb the cache: the graph restores it
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, e), f"replay {r}: output {i} differs"
