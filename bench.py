@@ -333,9 +333,18 @@ def bench_kvcache_prefill(torch, sa, W, steps, warmup):
         sa.kvcache_prefill(qc, q, kn, vn, seen, wl.scale, sink, out=o)
 
     ms8, _ = Timer(torch).run(step_q8, steps, warmup)
+    # appending the same chunk afterwards (every token lands: chunk <= window);
+    # bytes: the chunk's K, V read once, their slots written once
+    rows = wl.batch * wl.chunk * wl.hkv
+    app = {}
+    for name, c_, wbytes in (("bf16", cache, rows * wl.d * 2 * 2), ("q8", qc, rows * (wl.d + 4) * 2)):
+        ms_a, _ = Timer(torch).run(lambda: sa.kvcache_append(c_, kn, vn, seen), steps, warmup)
+        nb = rows * wl.d * 2 * 2 + wbytes
+        app[name] = {"ms": round(ms_a, 4), "GBs": round(nb / (ms_a * 1e-3) / 1e9, 1), "bytes": nb}
     return {"workload": "streaming_chunked_prefill", "unit": "TFLOP/s", "value": round(tf, 2),
             "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_step": round(ms, 4),
             "q8_cache": {"ms": round(ms8, 4), "tflops": round(flops / (ms8 * 1e-3) / 1e12, 2)},
+            "append": app,
             "valid_pairs": pairs,
             "config": {"batch": wl.batch, "chunk": wl.chunk, "n_sink": wl.n_sink, "window": wl.window,
                        "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.d, "cache": "bf16"}}

@@ -19,23 +19,24 @@ namespace kvc {
 
 constexpr float kE4m3Max = 448.f;
 
-// One wavefront per (sequence b, chunk token c, KV head g): writes the K and
-// V rows of the token to its slot, or nothing when a later token of the same
-// chunk takes that slot (only the last `window` non-first tokens survive, so
-// no slot gets two writers).
+// 16 lanes per (sequence b, chunk token c, KV head g), 16-byte pieces: writes
+// the K and V rows of the token to its slot, or nothing when a later token of
+// the same chunk takes that slot (only the last `window` non-first tokens
+// survive, so no slot gets two writers).
 template <bool QUANT>
-__global__ __launch_bounds__(64) void append_kernel(KvCache c, const uint16_t* __restrict__ k_new,
-                                                    const uint16_t* __restrict__ v_new, int chunk,
-                                                    const int32_t* __restrict__ n_seen) {
-  const int g = blockIdx.x % c.hkv;
-  const int tok = blockIdx.x / c.hkv;
-  const int cc = tok % chunk;
-  const int b = tok / chunk;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void append_kernel(KvCache c, const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new, int chunk,
+                                                     const int32_t* __restrict__ n_seen) {
+  const size_t unit = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (unit >= static_cast<size_t>(c.batch) * chunk * c.hkv) return;
+  const int g = static_cast<int>(unit % c.hkv);
+  const int cc = static_cast<int>((unit / c.hkv) % chunk);
+  const int b = static_cast<int>(unit / (static_cast<size_t>(c.hkv) * chunk));
   const int D = c.d;
   const long long p = static_cast<long long>(n_seen[b]) + cc;
   const long long total = static_cast<long long>(n_seen[b]) + chunk;
-  if (p >= c.n_sink && p < total - c.window) return;      // evicted within this chunk
+  if (p >= c.n_sink && p < total - c.window) return;      // evicted within this chunk (uniform per row)
   const size_t src = ((static_cast<size_t>(b) * chunk + cc) * c.hkv + g) * D;
   const bool is_sink = p < c.n_sink;
   const int ring = is_sink ? 0 : static_cast<int>((p - c.n_sink) % c.window);
@@ -53,45 +54,46 @@ __global__ __launch_bounds__(64) void append_kernel(KvCache c, const uint16_t* _
       dk = static_cast<uint16_t*>(c.sink_k) + dst;
       dv = static_cast<uint16_t*>(c.sink_v) + dst;
     }
-    for (int d = lane; d < D; d += 64) {
-      dk[d] = k_new[src + d];
-      dv[d] = v_new[src + d];
+    for (int e = sub; e < D / 8; e += 16) {
+      *reinterpret_cast<u32x4*>(dk + 8 * e) = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
+      *reinterpret_cast<u32x4*>(dv + 8 * e) = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
     }
     return;
   }
 
-  // 8-bit ring row: amax over the row, then the codes.
+  // 8-bit ring row (head_dim 128: 8 values per lane): amax over the row, then
+  // the codes, two per conversion.
   const size_t dst = ((static_cast<size_t>(b) * c.window + ring) * c.hkv + g) * D;
   const size_t sidx = (static_cast<size_t>(b) * c.hkv + g) * c.window + ring;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const uint16_t* x = (which == 0 ? k_new : v_new) + src;
-    float xv[4];
+    const u32x4 raw = *reinterpret_cast<const u32x4*>((which == 0 ? k_new : v_new) + src + 8 * sub);
+    float xv[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xv[2 * j] = __uint_as_float(raw[j] << 16);
+      xv[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
+    }
     float amax = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = lane + 64 * r;
-      xv[r] = d < D ? bf16_to_f32(x[d]) : 0.f;
-      amax = fmaxf(amax, fabsf(xv[r]));
-    }
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(xv[j]));
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
     const float scale = amax > 0.f ? amax / kE4m3Max : 0.f;
     const float inv = amax > 0.f ? kE4m3Max / amax : 0.f;
-    uint8_t* out = (which == 0 ? c.win_k : c.win_v) + dst;
+    u32x2 codes = {0u, 0u};
+    if (amax > 0.f) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = lane + 64 * r;
-      if (d < D) {
-        const float v = xv[r] * inv;
-        const int code = __builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false);
-        out[d] = static_cast<uint8_t>(amax > 0.f ? (code & 0xff) : 0);
+      for (int j = 0; j < 2; ++j) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(xv[4 * j] * inv, xv[4 * j + 1] * inv, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(xv[4 * j + 2] * inv, xv[4 * j + 3] * inv, w, true);
+        codes[j] = static_cast<uint32_t>(w);
       }
     }
-    if (lane == 0) (which == 0 ? c.win_k_scale : c.win_v_scale)[sidx] = scale;
+    *reinterpret_cast<u32x2*>((which == 0 ? c.win_k : c.win_v) + dst + 8 * sub) = codes;
+    if (sub == 0) (which == 0 ? c.win_k_scale : c.win_v_scale)[sidx] = scale;
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Chunked prefill against the cache.  Query row c of sequence b is stream
@@ -256,7 +258,7 @@ hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void
   const long long rows = static_cast<long long>(c.batch) * chunk * c.hkv;
   if (rows <= 0) return hipSuccess;
   auto kern = c.quantized ? kvc::append_kernel<true> : kvc::append_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(64), 0, st, c,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st, c,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), chunk,
                      n_seen);
   return hipGetLastError();
