@@ -202,7 +202,8 @@ typedef struct sink_attn_kvcache_desc {
  *   k_new, v_new  bfloat16 [B, chunk, Hkv, D]: the new tokens in stream order.
  *   n_seen        device int32 [B] (>= 0, n_seen[b] + chunk < 2^31): tokens
  *                 each stream held before this call; token c of sequence b
- *                 has stream position n_seen[b] + c.
+ *                 has stream position n_seen[b] + c (a negative count reads
+ *                 as 0).
  * Each token is written to its slot (quantized ring rows with their scales),
  * overwriting the token that slot held; a chunk token that a later token of
  * the same chunk would overwrite at once is not written, so no slot has two

@@ -34,8 +34,9 @@ __global__ __launch_bounds__(256) void append_kernel(KvCache c, const uint16_t* 
   const int cc = static_cast<int>((unit / c.hkv) % chunk);
   const int b = static_cast<int>(unit / (static_cast<size_t>(c.hkv) * chunk));
   const int D = c.d;
-  const long long p = static_cast<long long>(n_seen[b]) + cc;
-  const long long total = static_cast<long long>(n_seen[b]) + chunk;
+  const long long p0 = max(n_seen[b], 0);               // a negative count reads as an empty stream
+  const long long p = p0 + cc;
+  const long long total = p0 + chunk;
   if (p >= c.n_sink && p < total - c.window) return;      // evicted within this chunk (uniform per row)
   const size_t src = ((static_cast<size_t>(b) * chunk + cc) * c.hkv + g) * D;
   const bool is_sink = p < c.n_sink;

@@ -103,6 +103,17 @@ def test_decode_over_cache(quantized, splits):
 
 
 @pytest.mark.parametrize("quantized", [False, True])
+def test_decode_over_cache_without_first_tokens(quantized):
+    """n_sink = 0: the cache is the ring alone (no first-token chunk)."""
+    print(f"[case] kvcache decode n_sink=0 q={quantized}", flush=True)
+    rng = np.random.default_rng(16)
+    for chunks in ([3], [50, 90]):
+        cache, ref, seen = _stream(rng, 2, 2, 128, 0, 64, quantized, chunks)
+        for splits in (0, 3):
+            _check_decode(cache, ref, seen, 0, 64, 8, splits, rng)
+
+
+@pytest.mark.parametrize("quantized", [False, True])
 def test_decode_over_cache_odd_window_and_groups(quantized):
     """A ring length that is not a multiple of 4 (the 8-bit decode then reads
     scales one slot at a time), 5 first tokens, and 3 query heads per KV head."""
