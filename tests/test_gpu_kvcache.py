@@ -268,3 +268,34 @@ def test_prefill_fullsize_sampled():
     want = KO.cache_prefill(wl.q, ref, wl.k_new, wl.v_new, wl.n_seen, wl.n_sink, wl.window, wl.scale,
                             sink=wl.sink, rows=rows)
     _check_prefill_rows(got, want, rows)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_fullsize_q8_sampled():
+    """The bench's chunked prefill against the 8-bit cache (random e4m3 ring
+    codes, row scales of unit-normal size, the same chunk), sampled rows."""
+    print("[case] kvcache prefill fullsize q8", flush=True)
+    wl = W.kvcache_prefill()
+    rng = np.random.default_rng(25)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    ref = KO.new_cache(wl.batch, wl.n_sink, wl.window, wl.hkv, wl.d, quantized=True)
+    ref["sink_k"][:] = wl.k_cache[:, :wl.n_sink]
+    ref["sink_v"][:] = wl.v_cache[:, :wl.n_sink]
+    for name in ("win_k", "win_v"):
+        ref[name][:] = finite[rng.integers(0, len(finite), size=ref[name].shape)]
+    for name in ("win_k_scale", "win_v_scale"):
+        ref[name][:] = (rng.uniform(2.0, 4.0, size=ref[name].shape) / 448.0).astype(np.float32)
+    cache = sa.KvCache(wl.batch, wl.n_sink, wl.window, wl.hkv, wl.d, quantized=True)
+    for name in ("sink_k", "sink_v"):
+        getattr(cache, name).copy_(torch.from_numpy(ref[name]).to(torch.bfloat16))
+    for name in ("win_k", "win_v", "win_k_scale", "win_v_scale"):
+        getattr(cache, name).copy_(torch.from_numpy(ref[name]))
+    dev_ = lambda x: torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+    got = sa.kvcache_prefill(cache, dev_(wl.q), dev_(wl.k_new), dev_(wl.v_new),
+                             torch.from_numpy(wl.n_seen).to(DEV), wl.scale, torch.from_numpy(wl.sink).to(DEV))
+    torch.cuda.synchronize()
+    rows = [(int(b), int(c)) for b, c in zip(rng.integers(0, wl.batch, 8), rng.integers(0, wl.chunk, 8))]
+    rows += [(0, 0), (wl.batch - 1, wl.chunk - 1)]
+    want = KO.cache_prefill(wl.q, ref, wl.k_new, wl.v_new, wl.n_seen, wl.n_sink, wl.window, wl.scale,
+                            sink=wl.sink, rows=rows)
+    _check_prefill_rows(got, want, rows)
