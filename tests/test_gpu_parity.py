@@ -213,6 +213,10 @@ def test_bwd_is_repeatable():
 DECODE_CASES = {
     "d128_g8": dict(batch=5, slots=300, hq=16, hkv=2, d=128),
     "d128_g4_lens": dict(batch=4, slots=257, hq=8, hkv=2, d=128, cache_seqlens=[257, 1, 100, 64]),
+    # more than 16 query heads per KV head: two head groups per KV head (the
+    # second one partly empty with 20)
+    "d128_g20": dict(batch=2, slots=200, hq=40, hkv=2, d=128, cache_seqlens=[200, 37]),
+    "d128_g32": dict(batch=2, slots=130, hq=32, hkv=1, d=128),
     "d64": dict(batch=3, slots=100, hq=4, hkv=1, d=64),
     "f32": dict(batch=2, slots=70, hq=4, hkv=2, d=16, dtype="f32"),
     "no_sink": dict(batch=3, slots=200, hq=8, hkv=1, d=128, sink=False),
