@@ -299,3 +299,31 @@ def test_prefill_fullsize_q8_sampled():
     want = KO.cache_prefill(wl.q, ref, wl.k_new, wl.v_new, wl.n_seen, wl.n_sink, wl.window, wl.scale,
                             sink=wl.sink, rows=rows)
     _check_prefill_rows(got, want, rows)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_cache_calls_without_s(d):
+    """s is optional (a NULL pointer at the C ABI): the other outputs are the
+    same bits with and without it, for chunked prefill (the matrix-core and
+    the generic forward) and decode."""
+    print(f"[case] kvcache calls without s d={d}", flush=True)
+    rng = np.random.default_rng(26)
+    B, hq, hkv, n_sink, window, C = 2, 4, 2, 4, 40, 30
+    cache = sa.KvCache(B, n_sink, window, hkv, d, quantized=False)
+    seen = torch.tensor([5, 70], dtype=torch.int32, device=DEV)
+    _, kt = _bf16(rng, (B, 80, hkv, d))
+    _, vt = _bf16(rng, (B, 80, hkv, d))
+    sa.kvcache_append(cache, kt, vt, torch.zeros_like(seen))
+    _, qt = _bf16(rng, (B, C, hq, d))
+    _, knt = _bf16(rng, (B, C, hkv, d))
+    _, vnt = _bf16(rng, (B, C, hkv, d))
+    sink = torch.from_numpy(rng.standard_normal(hq).astype(np.float32)).to(DEV)
+    o1, l1, s1 = sa.kvcache_prefill(cache, qt, knt, vnt, seen, 0.1, sink)
+    o2, l2, s2 = sa.kvcache_prefill(cache, qt, knt, vnt, seen, 0.1, sink, return_s=False)
+    assert s2 is None and s1 is not None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if d == 128:
+        _, q1 = _bf16(rng, (B, hq, d))
+        a = sa.kvcache_decode(cache, q1, seen, 0.1, sink)
+        b = sa.kvcache_decode(cache, q1, seen, 0.1, sink, return_s=False)
+        assert b[2] is None and torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
