@@ -57,7 +57,7 @@ import numpy as np
 __all__ = [
     "kv_head", "sample_mask", "fwd", "fwd_virtual_key", "bwd", "decode",
     "fwd_rows", "bwd_rows", "bwd_kv_rows", "logsumexp_rows", "first_token_gate",
-    "first_token_gate_rows", "head_importance",
+    "first_token_gate_rows", "head_importance", "mask_rows", "fwd_bwd_heads",
 ]
 
 
@@ -79,18 +79,24 @@ def sample_mask(L, n_sink, window, blocks=None, block_size=64):
     ``blocks``: None, or an int array [nqb, KB] of selected sample-local KV
     block ids per sample-local query block (-1 = padding).
     """
-    i = np.arange(L)[:, None]
-    j = np.arange(L)[None, :]
+    return mask_rows(0, L, np.arange(L), n_sink, window, blocks, block_size)
+
+
+def mask_rows(i0, i1, cols, n_sink, window, blocks=None, block_size=64):
+    """The valid-key predicate of sample_mask for sample-local query rows
+    [i0, i1) and the sample-local key indices ``cols``: [i1 - i0, len(cols)]."""
+    i = np.arange(i0, i1)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
     m = j <= i                                   # causal order
     if window > 0:                               # kept first tokens + recent window
         m = m & ((j < n_sink) | (i - j < window))
     if blocks is not None:                       # sparse block selection
-        sel = np.zeros((L, L), dtype=bool)
-        for qb in range(blocks.shape[0]):
-            r0, r1 = qb * block_size, min(L, (qb + 1) * block_size)
+        sel = np.zeros(m.shape, dtype=bool)
+        for qb in range(i0 // block_size, (i1 - 1) // block_size + 1):
+            r0, r1 = max(i0, qb * block_size) - i0, min(i1, (qb + 1) * block_size) - i0
             for kb in blocks[qb]:
                 if kb >= 0:
-                    sel[r0:r1, kb * block_size:(kb + 1) * block_size] = True
+                    sel[r0:r1] |= (j[0] // block_size) == kb
         m = m & sel
     return m
 
@@ -374,22 +380,6 @@ def _row_state(q, k, v, cu, qoff, t, h, scale, n_sink, window, block_indices, bl
     return keys, g, p, o, lorig, s
 
 
-def _pair_visible(cu, qoff, t, tj, g, n_sink, window, block_indices, block_size):
-    """Whether key token tj is valid for query token t and KV head g (the
-    same definition as sample_mask, for one pair)."""
-    b = int(np.searchsorted(cu, t, side="right") - 1)
-    if not (cu[b] <= tj <= t):
-        return False
-    i, j = t - int(cu[b]), tj - int(cu[b])
-    if window > 0 and not (j < n_sink or i - j < window):
-        return False
-    if block_indices is not None:
-        row = np.asarray(block_indices[qoff[b] + i // block_size, g])
-        if not np.any(row == j // block_size):
-            return False
-    return True
-
-
 def fwd_rows(q, k, v, cu_seqlens, scale, rows, n_sink=0, window=0, block_indices=None,
              block_size=64, sink=None):
     """Forward for the given (token, head) pairs only: (O [n,D], lse [n], s [n])."""
@@ -457,39 +447,121 @@ def bwd_rows(q, k, v, cu_seqlens, scale, do, rows, n_sink=0, window=0, block_ind
     return np.array(dqs), np.array(deltas), np.array(oms)
 
 
+def _slab_columns(i0, i1, n_sink, window, blocks, block_size):
+    """Sample-local keys that rows [i0, i1) might see: the causal keys [0, i1),
+    narrowed to the kept first tokens plus [i0 - window + 1, i1) with a window
+    and to the rows' selected blocks with block lists.  Only a superset is
+    needed: mask_rows is applied on top."""
+    cols = np.arange(i1, dtype=np.int64)
+    if window > 0:
+        cols = cols[(cols < n_sink) | (cols > i0 - window)]
+    if blocks is not None:
+        sel = set()
+        for qb in range(i0 // block_size, (i1 - 1) // block_size + 1):
+            sel.update(int(kb) for kb in blocks[qb] if kb >= 0)
+        cols = cols[np.isin(cols // block_size, np.array(sorted(sel), dtype=np.int64))]
+    return cols
+
+
+def _slab(q, k, v, do, t0, i0, i1, h, g, scale, n_sink, window, blocks, block_size, a):
+    """The forward and backward quantities of sample-local query rows
+    [i0, i1) of one head (the sample starting at packed row t0), over the keys
+    they can see: the same steps as fwd and bwd on that slab of the masked
+    score matrix.  Returns (cols, P, dS, O, L_orig, s, Delta)."""
+    cols = _slab_columns(i0, i1, n_sink, window, blocks, block_size)
+    M = mask_rows(i0, i1, cols, n_sink, window, blocks, block_size)
+    Q = np.asarray(q[t0 + i0:t0 + i1, h], dtype=np.float64)
+    K = np.asarray(k[t0 + cols, g], dtype=np.float64)
+    V = np.asarray(v[t0 + cols, g], dtype=np.float64)
+    x = np.where(M, scale * (Q @ K.T), -np.inf)
+    lorig = logsumexp_rows(x)
+    lnew, s, _ = _sink_terms(lorig, None if a is None else a[h])
+    safe = np.where(np.isfinite(lnew), lnew, 0.0)
+    P = np.where(M, np.exp(x - safe[:, None]), 0.0)
+    O = P @ V
+    dS = delta = None
+    if do is not None:
+        dO = np.asarray(do[t0 + i0:t0 + i1, h], dtype=np.float64)
+        delta = np.sum(dO * O, axis=1)
+        dS = P * (dO @ V.T - delta[:, None])
+    return cols, P, dS, O, lorig, s, delta
+
+
+def _slab_rows(block_indices):
+    """Rows per slab: one query block with block lists (each block has its own
+    selection), else 256."""
+    return 64 if block_indices is not None else 256
+
+
 def bwd_kv_rows(q, k, v, cu_seqlens, scale, do, kv_rows, n_sink=0, window=0,
                 block_indices=None, block_size=64, sink=None):
     """dK and dV rows for the given (key token, KV head) pairs.
 
     Each is a sum over every (query row, query head of the group) that sees
-    the key; every such query row is evaluated in full.
+    the key: dK_j = alpha sum dS_ij Q_i and dV_j = sum P_ij dO_i ([Notes] s8),
+    with every query row from the key on evaluated in slabs of rows (_slab).
     """
     a = _as64(sink)
-    hq, hkv = q.shape[1], k.shape[1]
+    hq, hkv, D = q.shape[1], k.shape[1], q.shape[2]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     qoff = _q_block_offsets(cu, block_size)
-    dks, dvs = [], []
-    for tj, g in kv_rows:
-        tj, g = int(tj), int(g)
-        b = int(np.searchsorted(cu, tj, side="right") - 1)
-        t1 = int(cu[b + 1])
-        dk_row = np.zeros(q.shape[2])
-        dv_row = np.zeros(q.shape[2])
+    dks = np.zeros((len(kv_rows), D))
+    dvs = np.zeros((len(kv_rows), D))
+    groups = {}
+    for n, (tj, g) in enumerate(kv_rows):
+        b = int(np.searchsorted(cu, int(tj), side="right") - 1)
+        groups.setdefault((b, int(g)), []).append((n, int(tj) - int(cu[b])))
+    rows_per = _slab_rows(block_indices)
+    for (b, g), items in groups.items():
+        t0, L = int(cu[b]), int(cu[b + 1] - cu[b])
+        blocks = _blocks_of(block_indices, qoff, b, g)
+        jmin = min(j for _, j in items)
         for h in range(hq):
             if kv_head(h, hq, hkv) != g:
                 continue
-            for t in range(tj, t1):
-                if not _pair_visible(cu, qoff, t, tj, g, n_sink, window, block_indices, block_size):
-                    continue
-                keys, _, p, o, _, _ = _row_state(q, k, v, cu, qoff, t, h, scale,
-                                                 n_sink, window, block_indices, block_size, a)
-                pj = p[np.nonzero(keys == tj)[0][0]]
-                dot = np.asarray(do[t, h], dtype=np.float64)
-                delta = float(dot @ o)
-                dpj = float(np.asarray(v[tj, g], dtype=np.float64) @ dot)
-                dsj = pj * (dpj - delta)
-                dk_row += scale * dsj * np.asarray(q[t, h], dtype=np.float64)
-                dv_row += pj * dot
-        dks.append(dk_row)
-        dvs.append(dv_row)
-    return np.array(dks), np.array(dvs)
+            for i0 in range(jmin - jmin % rows_per, L, rows_per):
+                i1 = min(L, i0 + rows_per)
+                cols, P, dS, _, _, _, _ = _slab(q, k, v, do, t0, i0, i1, h, g, scale, n_sink, window,
+                                                blocks, block_size, a)
+                Q = np.asarray(q[t0 + i0:t0 + i1, h], dtype=np.float64)
+                dO = np.asarray(do[t0 + i0:t0 + i1, h], dtype=np.float64)
+                for n, j in items:
+                    c = np.searchsorted(cols, j)
+                    if c < len(cols) and cols[c] == j:
+                        dks[n] += scale * (dS[:, c] @ Q)
+                        dvs[n] += P[:, c] @ dO
+    return dks, dvs
+
+
+def fwd_bwd_heads(q, k, v, cu_seqlens, scale, do, heads, n_sink=0, window=0, block_indices=None,
+                  block_size=64, sink=None):
+    """Every row of the given query heads: O_new, L_orig, s and Delta, and
+    dsink_h = -sum_i Delta_ih (1 - s_ih) ([Notes] s7, boxed equation), the
+    rows evaluated in slabs (_slab).  Returns (O [T,n,D], lse [T,n], s [T,n],
+    delta [T,n], dsink [n] or None)."""
+    a = _as64(sink)
+    T, hq, D = q.shape
+    hkv = k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    qoff = _q_block_offsets(cu, block_size)
+    n = len(heads)
+    o = np.zeros((T, n, D))
+    lse = np.full((T, n), -np.inf)
+    s_all = np.ones((T, n))
+    delta_all = np.zeros((T, n))
+    rows_per = _slab_rows(block_indices)
+    for x, h in enumerate(heads):
+        g = kv_head(int(h), hq, hkv)
+        for b in range(len(cu) - 1):
+            t0, L = int(cu[b]), int(cu[b + 1] - cu[b])
+            blocks = _blocks_of(block_indices, qoff, b, g)
+            for i0 in range(0, L, rows_per):
+                i1 = min(L, i0 + rows_per)
+                _, _, _, O, lorig, s, delta = _slab(q, k, v, do, t0, i0, i1, int(h), g, scale, n_sink,
+                                                    window, blocks, block_size, a)
+                o[t0 + i0:t0 + i1, x] = O
+                lse[t0 + i0:t0 + i1, x] = lorig
+                s_all[t0 + i0:t0 + i1, x] = s
+                delta_all[t0 + i0:t0 + i1, x] = delta
+    dsink = None if a is None else -np.sum(delta_all * (1.0 - s_all), axis=0)
+    return o, lse, s_all, delta_all, dsink

@@ -10,7 +10,8 @@ import oracle
 import streamingllm_sink_attn_amd as sa
 from streamingllm_sink_attn_amd import workloads as W
 
-from gpu_helpers import DEV, TOL_BF16, assert_lse, dev, host
+from gpu_helpers import (DEV, TOL_BF16, assert_dsink_per_head, assert_grad, assert_lse, dev,
+                         dsink_storage_floor, host)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
@@ -77,6 +78,27 @@ def test_gqa_prefill_full():
     _check_fwd_rows(wl, o, lse, s, _sample_rows(wl, 96, 1))
 
 
+def _check_kv_rows(wl, dk, dv, kv_rows, kw):
+    """dK / dV key rows against the oracle, every (query row, head) that sees
+    the key summed in float64."""
+    rdk, rdv = oracle.bwd_kv_rows(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, wl.do.f32,
+                                  kv_rows, **kw)
+    hdk, hdv = host(dk), host(dv)
+    got_k = np.stack([hdk[t, g] for t, g in kv_rows])
+    got_v = np.stack([hdv[t, g] for t, g in kv_rows])
+    assert_grad(got_k, rdk, TOL_BF16, f"dK rows {kv_rows}")
+    assert_grad(got_v, rdv, TOL_BF16, f"dV rows {kv_rows}")
+
+
+def _check_dsink_heads(wl, dsink, heads, kw):
+    """dsink of whole heads against the oracle's sum over every row of the
+    head, head by head (bound: 1e-2 relative plus the bf16 storage of O)."""
+    ro, rl, _, _, rds = oracle.fwd_bwd_heads(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale,
+                                             wl.do.f32, heads, **kw)
+    floor = dsink_storage_floor(ro, wl.do.f32[:, heads], rl, wl.sink[heads], "bf16")
+    assert_dsink_per_head(host(dsink)[heads], rds, TOL_BF16, floor)
+
+
 def test_streaming_prefill_full_fwd_bwd():
     wl = W.streaming_prefill()
     _announce("streaming prefill fwd+bwd full")
@@ -92,18 +114,22 @@ def test_streaming_prefill_full_fwd_bwd():
     rdq, _, _ = oracle.bwd_rows(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, wl.do.f32,
                                 rows[:24], **kw)
     hdq = host(dq)
-    err = np.max(np.abs(np.stack([hdq[t, h] for t, h in rows[:24]]) - rdq))
-    assert err <= TOL_BF16["grad"], f"dQ err {err:.3e}"
-    # keys: a kept first token (seen by the whole sample), window keys, a tail key
+    assert_grad(np.stack([hdq[t, h] for t, h in rows[:24]]), rdq, TOL_BF16, "dQ rows")
+    # Keys: in every sample a kept first token and another key of the first
+    # 64-key tile (seen by every query of the sample: the split tiles whose
+    # float32 partials are added atomically), plus a window key; and the last
+    # key of the packed tensor.
     c = wl.cu_seqlens
-    kv_rows = [(int(c[3]) + 1, 5), (int(c[0]) + 2000, 0), (int(c[6]) + 700, 3), (int(c[8]) - 1, 7)]
-    rdk, rdv = oracle.bwd_kv_rows(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, wl.do.f32,
-                                  kv_rows, **kw)
-    hdk, hdv = host(dk), host(dv)
-    for n, (t, g) in enumerate(kv_rows):
-        assert np.max(np.abs(hdk[t, g] - rdk[n])) <= TOL_BF16["grad"], f"dK row {t}"
-        assert np.max(np.abs(hdv[t, g] - rdv[n])) <= TOL_BF16["grad"], f"dV row {t}"
+    kv_rows = []
+    for b in range(wl.batch):
+        g = b % wl.hkv
+        L = int(c[b + 1] - c[b])
+        kv_rows += [(int(c[b]) + b % wl.n_sink, g), (int(c[b]) + 5 + 7 * b, g),
+                    (int(c[b]) + L // 2 + b, g)]
+    kv_rows.append((int(c[wl.batch]) - 1, wl.hkv - 1))
+    _check_kv_rows(wl, dk, dv, kv_rows, kw)
     _dsink_property(wl, o, lse, do, dsink)
+    _check_dsink_heads(wl, dsink, [3, 30], kw)
 
 
 def test_streaming_prefill_full_visited_counts():
@@ -133,18 +159,19 @@ def test_block_sparse_full_fwd_bwd():
     rdq, _, _ = oracle.bwd_rows(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, wl.do.f32,
                                 rows[:16], **kw)
     hdq = host(dq)
-    err = np.max(np.abs(np.stack([hdq[t, h] for t, h in rows[:16]]) - rdq))
-    assert err <= TOL_BF16["grad"], f"dQ err {err:.3e}"
-    # keys in randomly selected (not first) blocks
+    assert_grad(np.stack([hdq[t, h] for t, h in rows[:16]]), rdq, TOL_BF16, "dQ rows")
+    # Keys: block 0 of every sample (selected by every query block: the most
+    # split key tiles) and keys of randomly selected blocks, one KV head per
+    # sample.
     c = wl.cu_seqlens
-    kv_rows = [(int(c[1]) + 64 * 200 + 5, 2), (int(c[2]) + 64 * 120 + 63, 6), (int(c[3]) + 64 * 250, 1)]
-    rdk, rdv = oracle.bwd_kv_rows(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, wl.do.f32,
-                                  kv_rows, **kw)
-    hdk, hdv = host(dk), host(dv)
-    for n, (t, g) in enumerate(kv_rows):
-        assert np.max(np.abs(hdk[t, g] - rdk[n])) <= TOL_BF16["grad"], f"dK row {t}"
-        assert np.max(np.abs(hdv[t, g] - rdv[n])) <= TOL_BF16["grad"], f"dV row {t}"
+    kv_rows = []
+    for b in range(wl.batch):
+        g = (2 * b + 1) % wl.hkv
+        kv_rows += [(int(c[b]), g), (int(c[b]) + 37, g), (int(c[b]) + 63, g),
+                    (int(c[b]) + 64 * (60 + 50 * b) + 5 * b, g), (int(c[b]) + 64 * (250 - 3 * b) + 63, g)]
+    _check_kv_rows(wl, dk, dv, kv_rows, kw)
     _dsink_property(wl, o, lse, do, dsink)
+    _check_dsink_heads(wl, dsink, [7, 60], kw)
 
 
 def test_block_sparse_full_visited_counts():

@@ -9,8 +9,9 @@ import oracle
 import streamingllm_sink_attn_amd as sa
 from streamingllm_sink_attn_amd import workloads as W
 
-from gpu_helpers import (DEV, assert_dsink, assert_grad, assert_lse, assert_out, check_fwd_full,
-                         dev, host, oracle_kwargs, prefill_args, run_bwd, run_fwd, tol_for)
+from gpu_helpers import (DEV, assert_dsink, assert_dsink_per_head, assert_grad, assert_lse, assert_out,
+                         check_fwd_full, dev, dsink_storage_floor, host, oracle_kwargs, prefill_args,
+                         run_bwd, run_fwd, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,23 +178,51 @@ BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "bl
              "window_g12"]
 
 
-@pytest.mark.parametrize("name", BWD_CASES)
-def test_bwd_bf16_variants(name):
-    wl = _wl(name)
-    _announce(f"bwd {name}")
+def _check_bwd(wl):
     args = prefill_args(wl)
     o, lse, s = run_fwd(wl, args)
     dq, dk, dv, dsink = run_bwd(wl, o, lse, args)
+    kw = oracle_kwargs(wl)
     rdq, rdk, rdv, rds = oracle.bwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale,
-                                    wl.do.f32, **oracle_kwargs(wl))
+                                    wl.do.f32, **kw)
     tol = tol_for(wl.dtype)
     assert_grad(host(dq), rdq, tol, "dQ")
     assert_grad(host(dk), rdk, tol, "dK")
     assert_grad(host(dv), rdv, tol, "dV")
     if wl.sink is not None:
+        ro, rl, _ = oracle.fwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, **kw)
         assert_dsink(host(dsink), rds, tol)
+        floor = dsink_storage_floor(ro, wl.do.f32, rl, wl.sink, wl.dtype)
+        assert_dsink_per_head(host(dsink), rds, tol, floor)
     else:
         assert dsink is None
+
+
+@pytest.mark.parametrize("name", BWD_CASES)
+def test_bwd_bf16_variants(name):
+    wl = _wl(name)
+    _announce(f"bwd {name}")
+    _check_bwd(wl)
+
+
+def _sink_values(kind, hq):
+    if kind == "mixed":
+        return np.array([(-20.0, 0.0, 20.0)[h % 3] for h in range(hq)], np.float32)
+    return np.full(hq, float(kind), np.float32)
+
+
+@pytest.mark.parametrize("kind", ["0", "20", "-20", "mixed"])
+@pytest.mark.parametrize("name", ["window_sink4", "blocks_g4", "dense_g4", "d64_generic"])
+def test_bwd_extreme_sinks(name, kind):
+    """The backward where p_sink matters most ("Attention Sink, Learnable Sink
+    and dsink" s10 lists an extreme sink among the cases to validate): a = 0,
+    a = +20 (s -> 0, O -> 0, p_sink -> 1), a = -20 (s -> 1, where 1 - s
+    cancels and p_sink = exp(a - L_new) keeps its precision), and the three
+    mixed across heads; dsink checked head by head."""
+    wl = _wl(name, seed=11)
+    wl.sink = _sink_values(kind, wl.hq)
+    _announce(f"bwd extreme sink {name} a={kind}")
+    _check_bwd(wl)
 
 
 def test_bwd_is_repeatable():

@@ -437,11 +437,42 @@ def test_row_evaluators_match_full():
             np.testing.assert_allclose(rl[n], lse[t, h], atol=1e-13)
             np.testing.assert_allclose(rs[n], s[t, h], atol=1e-13)
             np.testing.assert_allclose(rdq[n], dq[t, h], atol=1e-12)
-        kv_rows = [(0, 0), (3, 1), (40, 0), (70, 1), (114, 0)]
+        kv_rows = [(0, 0), (3, 1), (40, 0), (70, 1), (114, 0), (1, 0), (69, 1)]
         rdk, rdv = oracle.bwd_kv_rows(q, k, v, cu, 0.5, do, kv_rows, sink=a, **mask)
         for n, (t, g) in enumerate(kv_rows):
             np.testing.assert_allclose(rdk[n], dk[t, g], atol=1e-12)
             np.testing.assert_allclose(rdv[n], dv[t, g], atol=1e-12)
+        heads = [3, 0, 2]
+        ho, hl, hs, hdelta, hds = oracle.fwd_bwd_heads(q, k, v, cu, 0.5, do, heads, sink=a, **mask)
+        for x, h in enumerate(heads):
+            np.testing.assert_allclose(ho[:, x], o[:, h], atol=1e-13)
+            np.testing.assert_allclose(hl[:, x], lse[:, h], atol=1e-13)
+            np.testing.assert_allclose(hs[:, x], s[:, h], atol=1e-13)
+            np.testing.assert_allclose(hdelta[:, x], np.sum(do[:, h] * o[:, h], axis=1), atol=1e-12)
+            np.testing.assert_allclose(hds[x], dsink[h], rtol=1e-12, atol=1e-12)
+
+
+def test_row_evaluators_match_full_long_rows():
+    """Rows past one slab (256 rows; 64 with block lists): the slab evaluators
+    against the full oracle, with windows, kept tokens and block lists."""
+    rng = np.random.default_rng(15)
+    lengths = (600, 290)
+    T, hq, hkv, d = sum(lengths), 2, 1, 8
+    q, k, v = _rand(rng, T, hq, d), _rand(rng, T, hkv, d), _rand(rng, T, hkv, d)
+    do = _rand(rng, T, hq, d)
+    a = _rand(rng, hq)
+    cu = W.cu_from_lengths(lengths)
+    bi = W.sparse_block_lists(rng, lengths, hkv, n_random=3, block=64)
+    for mask in (dict(n_sink=4, window=100), dict(block_indices=bi, block_size=64),
+                 dict(n_sink=0, window=300), dict()):
+        _, dk, dv, dsink = oracle.bwd(q, k, v, cu, 0.5, do, sink=a, **mask)
+        kv_rows = [(0, 0), (2, 0), (64, 0), (299, 0), (599, 0), (600, 0), (700, 0), (889, 0)]
+        rdk, rdv = oracle.bwd_kv_rows(q, k, v, cu, 0.5, do, kv_rows, sink=a, **mask)
+        for n, (t, g) in enumerate(kv_rows):
+            np.testing.assert_allclose(rdk[n], dk[t, g], atol=1e-12)
+            np.testing.assert_allclose(rdv[n], dv[t, g], atol=1e-12)
+        *_, hds = oracle.fwd_bwd_heads(q, k, v, cu, 0.5, do, [1, 0], sink=a, **mask)
+        np.testing.assert_allclose(hds, dsink[[1, 0]], rtol=1e-12, atol=1e-12)
 
 
 # ---------------------------------------------------------------------------
