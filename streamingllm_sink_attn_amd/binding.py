@@ -1,16 +1,30 @@
 """Thin Python binding over libsinkattn.so (ctypes).
 
 Argument marshalling only: every step runs in the library's HIP kernels.
-PyTorch provides device memory (outputs and workspace) and the current stream.
-If the library is not built the calls raise; there is no fallback.
+PyTorch provides device memory (outputs and workspace) and streams.  If the
+library is not built the calls raise; there is no fallback.
+
+Streams: every call takes ``stream=`` (default: the current stream).  Outputs
+and workspace are allocated while that stream is current, so torch's caching
+allocator ties them to the stream the kernels run on and cannot hand the
+workspace to other work before those kernels finish.
+
+Debug checks: with the environment variable SINK_ATTN_DEBUG=1 every call
+first copies its index arrays (cu_seqlens, block_indices, cache lengths,
+stream positions) to the host and checks the device-side preconditions the C
+ABI documents but does not check (it never reads device memory from the
+host), raising SinkAttnError on a violation.  This synchronises, so it is
+for debugging only.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -141,6 +155,33 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+PEAKS_LIB_PATH = os.path.join(_HERE, "libsinkattn_peaks.so")
+_peaks = None
+
+PEAKS_SIGS = {
+    "sink_attn_peaks_read": (c_i32, [c_vp, ctypes.c_size_t, c_vp, c_i32, c_vp]),
+    "sink_attn_peaks_mfma": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
+    "sink_attn_peaks_exp": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
+}
+
+
+def peaks_lib() -> ctypes.CDLL:
+    """The microbenchmark library (include/sink_attn_peaks.h); raises if it
+    has not been built."""
+    global _peaks
+    if _peaks is None:
+        if not os.path.exists(PEAKS_LIB_PATH):
+            raise RuntimeError(f"{PEAKS_LIB_PATH} is missing: build it with "
+                               "`python -m streamingllm_sink_attn_amd.build`")
+        h = ctypes.CDLL(PEAKS_LIB_PATH)
+        for name, (res, args) in PEAKS_SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _peaks = h
+    return _peaks
+
+
 def _check(status: int):
     if status != OK:
         detail = lib().sink_attn_last_error().decode()
@@ -163,6 +204,95 @@ def _stream(stream) -> c_vp:
     if stream is None:
         stream = torch.cuda.current_stream()
     return c_vp(stream.cuda_stream)
+
+
+@contextlib.contextmanager
+def _on_stream(stream):
+    """Makes ``stream`` current for the allocations of one call (a no-op for
+    the current stream): outputs and workspace then belong to the stream
+    the kernels are enqueued on."""
+    if stream is None:
+        yield None
+    else:
+        with torch.cuda.stream(stream):
+            yield stream
+
+
+# ---------------------------------------------------------------------------
+# Host-side precondition checks (SINK_ATTN_DEBUG=1)
+# ---------------------------------------------------------------------------
+
+def debug_enabled() -> bool:
+    return os.environ.get("SINK_ATTN_DEBUG", "") == "1"
+
+
+def _host_ints(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu").numpy()
+    return np.asarray(x).astype(np.int64)
+
+
+def _bad(msg: str):
+    raise SinkAttnError(INVALID_ARGUMENT, f"precondition: {msg}")
+
+
+def check_prefill_preconditions(cu_seqlens, total_tokens: int, max_seqlen: int,
+                                block_indices=None, block_size: int = BLOCK_SIZE) -> None:
+    """The device-side preconditions of a packed prefill call: cu_seqlens[0] =
+    0, nondecreasing, cu_seqlens[batch] = total_tokens, every length <=
+    max_seqlen; with block lists, num_q_blocks >= sum_b ceil(L_b / 64) and
+    every entry of sample b's rows in [-1, ceil(L_b / 64))."""
+    cu = _host_ints(cu_seqlens).reshape(-1)
+    if cu.size == 0:
+        _bad("cu_seqlens is empty (it holds batch + 1 entries)")
+    if cu[0] != 0:
+        _bad(f"cu_seqlens[0] = {cu[0]}, must be 0")
+    lengths = np.diff(cu)
+    if np.any(lengths < 0):
+        b = int(np.nonzero(lengths < 0)[0][0])
+        _bad(f"cu_seqlens decreases at sample {b} ({cu[b]} -> {cu[b + 1]})")
+    if cu[-1] != int(total_tokens):
+        _bad(f"cu_seqlens[batch] = {cu[-1]} != total_tokens = {total_tokens}")
+    if lengths.size and int(lengths.max()) > int(max_seqlen):
+        b = int(np.argmax(lengths))
+        _bad(f"sample {b} has length {int(lengths[b])} > max_seqlen = {max_seqlen}")
+    if block_indices is None:
+        return
+    bi = _host_ints(block_indices)
+    if bi.ndim != 3:
+        _bad("block_indices must be [num_q_blocks, num_kv_heads, max_blocks]")
+    nqb = -(-lengths // block_size)
+    if bi.shape[0] < int(nqb.sum()):
+        _bad(f"block_indices has {bi.shape[0]} rows < sum_b ceil(L_b / {block_size}) = {int(nqb.sum())}")
+    off = 0
+    for b, n in enumerate(nqb):
+        rows = bi[off:off + int(n)]
+        if rows.size and (rows.min() < -1 or rows.max() >= n):
+            _bad(f"sample {b}: block ids must be in [-1, {int(n)}), found "
+                 f"[{int(rows.min())}, {int(rows.max())}]")
+        off += int(n)
+
+
+def check_decode_preconditions(cache_seqlens, slots: int) -> None:
+    """1 <= cache_seqlens[b] <= slots for every sequence."""
+    if cache_seqlens is None:
+        return
+    c = _host_ints(cache_seqlens).reshape(-1)
+    if c.size and (c.min() < 1 or c.max() > int(slots)):
+        b = int(np.argmin(c)) if c.min() < 1 else int(np.argmax(c))
+        _bad(f"cache_seqlens[{b}] = {int(c[b])} outside [1, {slots}]")
+
+
+def check_stream_positions(counts, name: str, chunk: int = 0) -> None:
+    """Stream positions of the rolling cache: counts[b] >= 0 and
+    counts[b] + chunk < 2^31."""
+    c = _host_ints(counts).reshape(-1)
+    if c.size and c.min() < 0:
+        b = int(np.argmin(c))
+        _bad(f"{name}[{b}] = {int(c[b])} < 0")
+    if c.size and int(c.max()) + int(chunk) >= 2 ** 31:
+        b = int(np.argmax(c))
+        _bad(f"{name}[{b}] + chunk = {int(c[b]) + int(chunk)} >= 2^31")
 
 
 def _need_cuda(*ts):
@@ -215,31 +345,35 @@ def fwd(q, k, v, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, wind
     """
     _need_cuda(q, k, v, cu_seqlens, block_indices, learnable_sink)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    desc = prefill_desc(q, k, cu_seqlens, _max_seqlen(cu_seqlens, max_seqlen), scale, n_sink, window,
-                        block_indices, learnable_sink)
+    ms = _max_seqlen(cu_seqlens, max_seqlen)
+    desc = prefill_desc(q, k, cu_seqlens, ms, scale, n_sink, window, block_indices, learnable_sink)
+    if debug_enabled():
+        check_prefill_preconditions(cu_seqlens, q.shape[0], ms, block_indices)
     T, hq, _ = q.shape
-    o = out if out is not None else torch.empty_like(q)
-    lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
-    s = torch.empty((T, hq), dtype=torch.float32, device=q.device) if return_s else None
-    L = lib()
-    ws_bytes = L.sink_attn_fwd_workspace_size(ctypes.byref(desc))
-    ws = _workspace(ws_bytes, q.device)
-    if gate0 is None:
-        _check(L.sink_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
-                               _p(ws), ws_bytes, _stream(stream)))
-    else:
-        _need_cuda(gate0)
-        if gate0.dtype != torch.float32 or tuple(gate0.shape) != (T, hq):
-            raise SinkAttnError(INVALID_ARGUMENT, "gate0 must be float32 [T, Hq]")
-        _check(L.sink_attn_fwd_gated(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
-                                     _p(gate0), _p(ws), ws_bytes, _stream(stream)))
+    with _on_stream(stream):
+        o = out if out is not None else torch.empty_like(q)
+        lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+        s = torch.empty((T, hq), dtype=torch.float32, device=q.device) if return_s else None
+        L = lib()
+        ws_bytes = L.sink_attn_fwd_workspace_size(ctypes.byref(desc))
+        ws = _workspace(ws_bytes, q.device)
+        if gate0 is None:
+            _check(L.sink_attn_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(s),
+                                   _p(ws), ws_bytes, _stream(stream)))
+        else:
+            _need_cuda(gate0)
+            if gate0.dtype != torch.float32 or tuple(gate0.shape) != (T, hq):
+                raise SinkAttnError(INVALID_ARGUMENT, "gate0 must be float32 [T, Hq]")
+            _check(L.sink_attn_fwd_gated(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse),
+                                         _p(s), _p(gate0), _p(ws), ws_bytes, _stream(stream)))
     return o, lse, s
 
 
 def fwd_gated(q, k, v, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,
               block_indices=None, learnable_sink=None, return_s=True, out=None, stream=None):
     """Forward plus the first-token gate.  Returns (o, lse, s or None, gate0 [T,Hq] float32)."""
-    gate0 = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    with _on_stream(stream):
+        gate0 = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     o, lse, s = fwd(q, k, v, cu_seqlens, max_seqlen, softmax_scale, n_sink, window, block_indices,
                     learnable_sink, return_s, out, stream, gate0=gate0)
     return o, lse, s, gate0
@@ -251,12 +385,13 @@ def head_importance(gate, out=None, stream=None):
     if gate.dtype != torch.float32 or gate.dim() != 2:
         raise SinkAttnError(INVALID_ARGUMENT, "gate must be float32 [rows, heads]")
     rows, heads = int(gate.shape[0]), int(gate.shape[1])
-    imp = out if out is not None else torch.empty(heads, dtype=torch.float32, device=gate.device)
-    L = lib()
-    ws_bytes = L.sink_attn_head_importance_workspace_size(rows, heads)
-    ws = _workspace(ws_bytes, gate.device)
-    _check(L.sink_attn_head_importance(_p(gate), rows, heads, _p(imp), _p(ws), ws_bytes,
-                                       _stream(stream)))
+    with _on_stream(stream):
+        imp = out if out is not None else torch.empty(heads, dtype=torch.float32, device=gate.device)
+        L = lib()
+        ws_bytes = L.sink_attn_head_importance_workspace_size(rows, heads)
+        ws = _workspace(ws_bytes, gate.device)
+        _check(L.sink_attn_head_importance(_p(gate), rows, heads, _p(imp), _p(ws), ws_bytes,
+                                           _stream(stream)))
     return imp
 
 
@@ -265,16 +400,19 @@ def bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen=None, softmax_scale=None, 
     """Backward.  Returns (dq, dk, dv, dsink float32 [Hq] or None)."""
     _need_cuda(q, k, v, o, lse, dout, cu_seqlens, block_indices, learnable_sink)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    desc = prefill_desc(q, k, cu_seqlens, _max_seqlen(cu_seqlens, max_seqlen), scale, n_sink, window,
-                        block_indices, learnable_sink)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dsink = (torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
-             if learnable_sink is not None else None)
-    L = lib()
-    ws_bytes = L.sink_attn_bwd_workspace_size(ctypes.byref(desc))
-    ws = _workspace(ws_bytes, q.device)
-    _check(L.sink_attn_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout),
-                           _p(dq), _p(dk), _p(dv), _p(dsink), _p(ws), ws_bytes, _stream(stream)))
+    ms = _max_seqlen(cu_seqlens, max_seqlen)
+    desc = prefill_desc(q, k, cu_seqlens, ms, scale, n_sink, window, block_indices, learnable_sink)
+    if debug_enabled():
+        check_prefill_preconditions(cu_seqlens, q.shape[0], ms, block_indices)
+    with _on_stream(stream):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsink = (torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
+                 if learnable_sink is not None else None)
+        L = lib()
+        ws_bytes = L.sink_attn_bwd_workspace_size(ctypes.byref(desc))
+        ws = _workspace(ws_bytes, q.device)
+        _check(L.sink_attn_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout),
+                               _p(dq), _p(dk), _p(dv), _p(dsink), _p(ws), ws_bytes, _stream(stream)))
     return dq, dk, dv, dsink
 
 
@@ -295,15 +433,18 @@ def decode(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, learnabl
     _need_cuda(q, k_cache, v_cache, cache_seqlens, learnable_sink)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
     desc = decode_desc(q, k_cache, scale, cache_seqlens, learnable_sink, num_splits)
+    if debug_enabled():
+        check_decode_preconditions(cache_seqlens, int(k_cache.shape[1]))
     B, hq, _ = q.shape
-    o = out if out is not None else torch.empty_like(q)
-    lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
-    L = lib()
-    ws_bytes = L.sink_attn_decode_workspace_size(ctypes.byref(desc))
-    ws = _workspace(ws_bytes, q.device)
-    _check(L.sink_attn_decode(ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(o), _p(lse),
-                              _p(s), _p(ws), ws_bytes, _stream(stream)))
+    with _on_stream(stream):
+        o = out if out is not None else torch.empty_like(q)
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+        s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
+        L = lib()
+        ws_bytes = L.sink_attn_decode_workspace_size(ctypes.byref(desc))
+        ws = _workspace(ws_bytes, q.device)
+        _check(L.sink_attn_decode(ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(o), _p(lse),
+                                  _p(s), _p(ws), ws_bytes, _stream(stream)))
     return o, lse, s
 
 
@@ -366,6 +507,8 @@ def kvcache_append(cache: KvCache, k_new, v_new, n_seen, stream=None):
     for t, name in ((k_new, "k_new"), (v_new, "v_new")):
         _expect(t, (cache.batch, C, cache.hkv, cache.d), torch.bfloat16, name)
     _expect(n_seen, (cache.batch,), torch.int32, "n_seen")
+    if debug_enabled():
+        check_stream_positions(n_seen, "n_seen", C)
     desc = cache.desc()
     _check(lib().sink_attn_kvcache_append(ctypes.byref(desc), _p(k_new), _p(v_new),
                                           int(k_new.shape[1]), _p(n_seen), _stream(stream)))
@@ -383,16 +526,19 @@ def kvcache_decode(cache: KvCache, q, n_tokens, softmax_scale=None, learnable_si
     _expect(learnable_sink, (hq,), torch.float32, "learnable_sink")
     _expect(out, (B, hq, cache.d), torch.bfloat16, "out")
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    o = out if out is not None else torch.empty_like(q)
-    lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
-    s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
+    if debug_enabled():
+        check_stream_positions(n_tokens, "n_tokens")
     desc = cache.desc()
-    L = lib()
-    ws_bytes = L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(desc), hq, int(num_splits))
-    ws = _workspace(ws_bytes, q.device)
-    _check(L.sink_attn_kvcache_decode(ctypes.byref(desc), _p(q), hq, _p(n_tokens), float(scale),
-                                      _p(learnable_sink), int(num_splits), _p(o), _p(lse), _p(s),
-                                      _p(ws), ws_bytes, _stream(stream)))
+    with _on_stream(stream):
+        o = out if out is not None else torch.empty_like(q)
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+        s = torch.empty((B, hq), dtype=torch.float32, device=q.device) if return_s else None
+        L = lib()
+        ws_bytes = L.sink_attn_kvcache_decode_workspace_size(ctypes.byref(desc), hq, int(num_splits))
+        ws = _workspace(ws_bytes, q.device)
+        _check(L.sink_attn_kvcache_decode(ctypes.byref(desc), _p(q), hq, _p(n_tokens), float(scale),
+                                          _p(learnable_sink), int(num_splits), _p(o), _p(lse), _p(s),
+                                          _p(ws), ws_bytes, _stream(stream)))
     return o, lse, s
 
 
@@ -413,16 +559,19 @@ def kvcache_prefill(cache: KvCache, q, k_new, v_new, n_seen, softmax_scale=None,
     _expect(learnable_sink, (hq,), torch.float32, "learnable_sink")
     _expect(out, (B, C, hq, cache.d), torch.bfloat16, "out")
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
-    o = out if out is not None else torch.empty_like(q)
-    lse = torch.empty((B, C, hq), dtype=torch.float32, device=q.device)
-    s = torch.empty((B, C, hq), dtype=torch.float32, device=q.device) if return_s else None
+    if debug_enabled():
+        check_stream_positions(n_seen, "n_seen", C)
     desc = cache.desc()
-    L = lib()
-    ws_bytes = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(desc), C, hq)
-    ws = _workspace(ws_bytes, q.device)
-    _check(L.sink_attn_kvcache_prefill(ctypes.byref(desc), _p(q), hq, _p(k_new), _p(v_new), C, _p(n_seen),
-                                       float(scale), _p(learnable_sink), _p(o), _p(lse), _p(s), _p(ws),
-                                       ws_bytes, _stream(stream)))
+    with _on_stream(stream):
+        o = out if out is not None else torch.empty_like(q)
+        lse = torch.empty((B, C, hq), dtype=torch.float32, device=q.device)
+        s = torch.empty((B, C, hq), dtype=torch.float32, device=q.device) if return_s else None
+        L = lib()
+        ws_bytes = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(desc), C, hq)
+        ws = _workspace(ws_bytes, q.device)
+        _check(L.sink_attn_kvcache_prefill(ctypes.byref(desc), _p(q), hq, _p(k_new), _p(v_new), C,
+                                           _p(n_seen), float(scale), _p(learnable_sink), _p(o), _p(lse),
+                                           _p(s), _p(ws), ws_bytes, _stream(stream)))
     return o, lse, s
 
 
@@ -437,6 +586,7 @@ def debug_visit_map(q, k, cu_seqlens, max_seqlen, n_sink=0, window=0, block_indi
     Hkv * sum_{b'<b} L_b'^2, each [L_b, L_b] row-major per KV head."""
     desc = prefill_desc(q, k, cu_seqlens, max_seqlen, 1.0, n_sink, window, block_indices, None)
     nbytes = int(k.shape[1]) * int(max_seqlen) * int(q.shape[0])
-    out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().sink_attn_debug_visit_map(ctypes.byref(desc), _p(out), nbytes, _stream(stream)))
+    with _on_stream(stream):
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        _check(lib().sink_attn_debug_visit_map(ctypes.byref(desc), _p(out), nbytes, _stream(stream)))
     return out
