@@ -162,7 +162,8 @@ sa::Decode to_decode(const sink_attn_decode_desc* d) {
 }
 
 size_t decode_ws_bytes(const sa::Decode& p) {
-  if (!sa::decode_mfma_supported(p)) return 0;
+  // one split: the split kernel applies the sink epilogue and writes O itself
+  if (!sa::decode_mfma_supported(p) || p.splits <= 1) return 0;
   // per (sequence, query head, split): acc[D] + (m, l)
   return round_up(static_cast<size_t>(p.batch) * p.hq * p.splits * (p.d + 2) * 4);
 }

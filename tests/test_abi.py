@@ -21,6 +21,22 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(sink_attn_[a-z_]+)\s*\(", text)))
 
 
+def test_peaks_library_exports_every_declared_symbol():
+    text = open(os.path.join(ROOT, "include", "sink_attn_peaks.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(sink_attn_peaks_[a-z_]+)\s*\(", text)))
+    assert len(names) == 3
+    lib = B.peaks_lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.PEAKS_SIGS)
+    # invalid arguments are refused before anything is launched
+    assert lib.sink_attn_peaks_read(None, 16, FAKE, 1, None) == 1
+    assert lib.sink_attn_peaks_read(FAKE, 15, FAKE, 1, None) == 1
+    assert lib.sink_attn_peaks_mfma(0, FAKE, 1, None) == 1
+    assert lib.sink_attn_peaks_exp(5, None, 1, None) == 1
+
+
 def test_library_exports_every_declared_symbol():
     lib = B.lib()
     names = declared_functions()
@@ -130,6 +146,11 @@ def test_check_decode():
     need = L.sink_attn_decode_workspace_size(ctypes.byref(_ddesc()))
     if need:
         assert chk(_ddesc(), ws=need - 1) == B.WORKSPACE_TOO_SMALL
+    # one split writes O itself: no partials, no workspace
+    assert L.sink_attn_decode_workspace_size(ctypes.byref(_ddesc(num_splits=1))) == 0
+    need3 = L.sink_attn_decode_workspace_size(ctypes.byref(_ddesc(num_splits=3)))
+    assert need3 >= 4 * 8 * 3 * 130 * 4
+    assert chk(_ddesc(num_splits=3), ws=need3 - 1) == B.WORKSPACE_TOO_SMALL
 
 
 def test_prefill_path_selection():
