@@ -46,7 +46,8 @@
  *   - The library never allocates, frees or synchronises.  Work is enqueued
  *     on `stream` (a hipStream_t; NULL = the null stream).  Scratch memory is
  *     the caller's `workspace`, of at least the size the matching
- *     *_workspace_size() call returns; its contents on entry do not matter.
+ *     *_workspace_size() call returns; its contents on entry do not matter
+ *     (sink_attn_decode_noalloc uses a fixed static array instead).
  *   - No call reads device memory from the host.  Device-side preconditions
  *     (monotone cu_seqlens with cu_seqlens[0] = 0 and cu_seqlens[batch] =
  *     total_tokens, every length <= max_seqlen, block ids < the sample's block
@@ -347,6 +348,24 @@ int sink_attn_decode(const sink_attn_decode_desc* desc,
                      const void* q, const void* k_cache, const void* v_cache,
                      void* o, float* lse, float* s,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The same call and results as sink_attn_decode, with
+ * the split partials in a static device array the library holds on each GPU
+ * it runs on (SINK_ATTN_NOALLOC_SCRATCH_BYTES, kept until the process ends)
+ * instead of a caller workspace.  A problem whose sink_attn_decode_workspace_size
+ * exceeds that size returns SINK_ATTN_WORKSPACE_TOO_SMALL (lower num_splits,
+ * or use sink_attn_decode).  Every call on one GPU shares the array: calls
+ * that overlap on one GPU (other streams or threads) race on it and must be
+ * ordered by the caller.  The first call on a device looks the array up on
+ * that device (no allocation).
+ */
+#define SINK_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int sink_attn_decode_noalloc(const sink_attn_decode_desc* desc,
+                             const void* q, const void* k_cache, const void* v_cache,
+                             void* o, float* lse, float* s, void* stream);
 
 /* Workspace bytes each call needs for this problem (0 = none).  Pure host. */
 size_t sink_attn_fwd_workspace_size(const sink_attn_prefill_desc* desc);

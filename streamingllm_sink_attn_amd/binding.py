@@ -125,6 +125,7 @@ _SIGS = {
     "sink_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               c_vp, ctypes.c_size_t, c_vp]),
     "sink_attn_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "sink_attn_decode_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "sink_attn_fwd_workspace_size": (ctypes.c_size_t, [c_vp]),
     "sink_attn_bwd_workspace_size": (ctypes.c_size_t, [c_vp]),
     "sink_attn_decode_workspace_size": (ctypes.c_size_t, [c_vp]),
@@ -445,6 +446,29 @@ def decode(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, learnabl
         ws = _workspace(ws_bytes, q.device)
         _check(L.sink_attn_decode(ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(o), _p(lse),
                                   _p(s), _p(ws), ws_bytes, _stream(stream)))
+    return o, lse, s
+
+
+def decode_noalloc(q, k_cache, v_cache, cache_seqlens=None, softmax_scale=None, learnable_sink=None,
+                   num_splits=0, o=None, lse=None, s=None, stream=None):
+    """Decode through sink_attn_decode_noalloc: the library allocates nothing
+    (split partials in its static per-GPU scratch).  The caller passes the
+    outputs o [B,Hq,D], lse [B,Hq] float32 and s [B,Hq] float32 or None; when
+    omitted they are allocated here, before the call.  Returns (o, lse, s)."""
+    _need_cuda(q, k_cache, v_cache, cache_seqlens, learnable_sink, o, lse, s)
+    scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+    desc = decode_desc(q, k_cache, scale, cache_seqlens, learnable_sink, num_splits)
+    if debug_enabled():
+        check_decode_preconditions(cache_seqlens, int(k_cache.shape[1]))
+    B, hq, _ = q.shape
+    with _on_stream(stream):
+        o = o if o is not None else torch.empty_like(q)
+        lse = lse if lse is not None else torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    _expect(o, tuple(q.shape), q.dtype, "o")
+    _expect(lse, (B, hq), torch.float32, "lse")
+    _expect(s, (B, hq), torch.float32, "s")
+    _check(lib().sink_attn_decode_noalloc(ctypes.byref(desc), _p(q), _p(k_cache), _p(v_cache), _p(o),
+                                          _p(lse), _p(s), _stream(stream)))
     return o, lse, s
 
 

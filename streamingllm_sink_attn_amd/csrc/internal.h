@@ -127,6 +127,10 @@ hipError_t launch_kvcache_decode_q8(const Decode& p, const KvCache& c, const voi
                                     float* lse, float* s, float* ws, hipStream_t st);
 int kvcache_q8_auto_splits(const Decode& p, const KvCache& c);
 
+// Records the detail sink_attn_last_error() returns on this thread; returns
+// status.
+int set_last_error(int status, const char* fmt, ...);
+
 // Fill kernels (used instead of hipMemsetAsync so callers may capture graphs).
 hipError_t launch_fill_zero(float* ptr, size_t n, hipStream_t st);
 hipError_t launch_fill_zero_bytes(uint8_t* ptr, size_t n, hipStream_t st);

@@ -262,6 +262,16 @@ sa::Decode kvcache_decode_problem(const sink_attn_kvcache_desc* c, int32_t hq,
 
 }  // namespace
 
+namespace sa {
+int set_last_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+}  // namespace sa
+
 extern "C" {
 
 const char* sink_attn_strerror(int status) {
