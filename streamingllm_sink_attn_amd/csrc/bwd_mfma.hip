@@ -34,6 +34,7 @@
 //     so they overlap the whole current iteration.
 //     Per-lane LDS offsets are computed once and the loop is unrolled by two
 //     so buffer offsets are immediates.
+#include <algorithm>
 #include <type_traits>
 
 #include "qmajor.cuh"
@@ -104,7 +105,8 @@ __device__ __forceinline__ TileWork tile_work(const Prefill& p, const BwdWork& w
   return tw;
 }
 
-// Chunks per key tile (an empty tile still gets one, which writes zeros).
+// Chunks per key tile (an empty tile still gets one, which writes zeros),
+// and whether the tile is split over several chunks.
 __global__ __launch_bounds__(256) void plan_kernel(Prefill p, BwdWork w, int nkt, int nq) {
   const int ntiles = p.batch * nkt * p.hkv;
   const int ti = blockIdx.x * blockDim.x + threadIdx.x;
@@ -119,6 +121,15 @@ __global__ __launch_bounds__(256) void plan_kernel(Prefill p, BwdWork w, int nkt
     chunks = max(1, (n + kChunk - 1) / kChunk);
   }
   w.plan[ti + 1] = chunks;
+  w.split_slot[ti + 1] = chunks > 1 ? 1 : 0;
+}
+
+// After the split tiles are numbered (a scan of the flags): a split tile
+// without an accumulator slot runs as one chunk.
+__global__ __launch_bounds__(256) void plan_clamp_kernel(Prefill p, BwdWork w, int ntiles) {
+  const int ti = blockIdx.x * blockDim.x + threadIdx.x;
+  if (ti >= ntiles) return;
+  if (w.plan[ti + 1] > 1 && w.split_slot[ti] >= w.max_split) w.plan[ti + 1] = 1;
 }
 
 // Zero (before) and convert (after) the float32 accumulators of split tiles.
@@ -132,26 +143,29 @@ __global__ __launch_bounds__(256) void split_tiles_kernel(Prefill p, BwdWork w, 
   const int t0 = p.cu[t.b];
   const int L = p.cu[t.b + 1] - t0;
   const int rows = min(BN, L - t.kt * BN);
+  const float* dka = w.dk_acc + static_cast<size_t>(w.split_slot[ti]) * BN * D;
+  const float* dva = w.dv_acc + static_cast<size_t>(w.split_slot[ti]) * BN * D;
   // 8 consecutive dims per thread and step: two 16-byte float32 accesses and
   // one 16-byte bf16 store per tensor.
   for (int c = threadIdx.x; c < rows * (D / 8); c += blockDim.x) {
     const int r = c / (D / 8), d0 = (c % (D / 8)) * 8;
     const size_t o = (static_cast<size_t>(t0 + t.kt * BN + r) * p.hkv + t.g) * D + d0;
+    const size_t a = static_cast<size_t>(r) * D + d0;       // slot row r
     if (kConvert) {
-      const f32x4 k0 = *reinterpret_cast<const f32x4*>(w.dk_acc + o);
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(w.dk_acc + o + 4);
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(w.dv_acc + o);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(w.dv_acc + o + 4);
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(dka + a);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(dka + a + 4);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(dva + a);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(dva + a + 4);
       *reinterpret_cast<u32x4*>(dK + o) = u32x4{pack_bf16x2(k0[0], k0[1]), pack_bf16x2(k0[2], k0[3]),
                                                 pack_bf16x2(k1[0], k1[1]), pack_bf16x2(k1[2], k1[3])};
       *reinterpret_cast<u32x4*>(dV + o) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
                                                 pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
     } else {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(w.dk_acc + o) = z;
-      *reinterpret_cast<f32x4*>(w.dk_acc + o + 4) = z;
-      *reinterpret_cast<f32x4*>(w.dv_acc + o) = z;
-      *reinterpret_cast<f32x4*>(w.dv_acc + o + 4) = z;
+      *reinterpret_cast<f32x4*>(const_cast<float*>(dka) + a) = z;
+      *reinterpret_cast<f32x4*>(const_cast<float*>(dka) + a + 4) = z;
+      *reinterpret_cast<f32x4*>(const_cast<float*>(dva) + a) = z;
+      *reinterpret_cast<f32x4*>(const_cast<float*>(dva) + a + 4) = z;
     }
   }
 }
@@ -249,6 +263,8 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
     const int ti = lo;
     const int chunk = item - w.plan[ti];
     const bool split = (w.plan[ti + 1] - w.plan[ti]) > 1;
+    // a split tile's float32 accumulators: slot rows 0..63 = keys k0..k0+63
+    const size_t slot_base = split ? static_cast<size_t>(w.split_slot[ti]) * BN * D : 0;
     const TileId t = tile_of(p, nkt, nq, ti);
     const int b = t.b, kt = t.kt, g = t.g;
     const int t0 = p.cu[b];
@@ -467,9 +483,10 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
         if (key < L) {
           const size_t o = static_cast<size_t>(t0 + key) * kvs + g * D + dim;
           if (split) {
-            __hip_atomic_fetch_add(w.dk_acc + o, p.scale * dKacc[nt][i], __ATOMIC_RELAXED,
+            const size_t a = slot_base + static_cast<size_t>(key - k0) * D + dim;
+            __hip_atomic_fetch_add(w.dk_acc + a, p.scale * dKacc[nt][i], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(w.dv_acc + o, dVacc[nt][i], __ATOMIC_RELAXED,
+            __hip_atomic_fetch_add(w.dv_acc + a, dVacc[nt][i], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
           } else {
             dK[o] = f32_to_bf16(p.scale * dKacc[nt][i]);
@@ -494,6 +511,33 @@ int bwd_num_tiles(const Prefill& p) {
   return p.batch * nkt * p.hkv;
 }
 
+// A key tile splits when its iterations (query tiles or reverse-list entries
+// seeing it, times the G query heads of its group) exceed kChunk, i.e. when
+// more than cap = kChunk / G query tiles see it.
+int bwd_max_split_tiles(const Prefill& p) {
+  const long long ntiles = bwd_num_tiles(p);
+  const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
+  const int G = p.hq / p.hkv;
+  const long long cap = bwd128::kChunk / G;
+  long long bound = ntiles;
+  if (p.blocks != nullptr) {
+    // every reverse-list entry comes from one block_indices entry
+    bound = static_cast<long long>(p.nqb) * p.hkv * p.max_blocks / (cap + 1);
+  } else if (p.window > 0) {
+    // a tile holding no kept first token is seen by at most (62 + W) / 64 + 1
+    // query tiles; tiles holding kept tokens may split
+    const long long per_head = (62LL + p.window) / qm::BN + 1;
+    if (per_head <= cap) {
+      const long long sink_tiles = std::min<long long>(nkt, (p.n_sink + qm::BN - 1) / qm::BN);
+      bound = static_cast<long long>(p.batch) * p.hkv * sink_tiles;
+    }
+  } else {
+    // causal: tile kt of a sample is seen by nqt - kt <= nkt - kt query tiles
+    bound = static_cast<long long>(p.batch) * p.hkv * std::max<long long>(0, nkt - cap);
+  }
+  return static_cast<int>(std::min(ntiles, std::max(0LL, bound)));
+}
+
 hipError_t launch_bwd_dq(const Prefill& p, const void* q, const void* k, const void* v,
                          const void* dout, const BwdWork& w, void* dq, hipStream_t st);
 hipError_t launch_scan(int32_t* off, int n, hipStream_t st);
@@ -509,7 +553,10 @@ hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const
   uint16_t* dK = static_cast<uint16_t*>(dk);
   uint16_t* dV = static_cast<uint16_t*>(dv);
   hipLaunchKernelGGL(bwd128::plan_kernel, dim3((ntiles + 255) / 256), dim3(256), 0, st, p, w, nkt, nq);
-  hipError_t e = launch_scan(w.plan, ntiles, st);
+  hipError_t e = launch_scan(w.split_slot, ntiles, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd128::plan_clamp_kernel, dim3((ntiles + 255) / 256), dim3(256), 0, st, p, w, ntiles);
+  e = launch_scan(w.plan, ntiles, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd128::split_tiles_kernel<false>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,
                      dK, dV);

@@ -36,12 +36,14 @@ struct BwdWork {
   float* dsink_terms;// [T, Hq]  -Delta * p_sink per row
   float* dsink_part; // [ceil(T/64), Hq] per-slab partial sums of the terms
   float* dq_acc;     // [T, Hq, D]  (MFMA path) accumulated dQ
-  float* dk_acc;     // [T, Hkv, D] (generic path, and the MFMA path's split sink tiles)
-  float* dv_acc;     // [T, Hkv, D]
+  float* dk_acc;     // generic path: [T, Hkv, D]; MFMA path: [max split tiles, 64, D] (split key tiles)
+  float* dv_acc;     // as dk_acc
   int32_t* csr_off;  // [nqb*Hkv + 1]  (block mode) per (KV block, KV head) list offsets
   int32_t* csr_idx;  // [nqb*Hkv*max_blocks] query blocks selecting each KV block
   uint32_t* csr_bits;// [nqb*Hkv*words] selection bit matrix the lists are built from
   int32_t* plan;     // [batch*nkt*Hkv + 1] (MFMA path) chunks per key tile -> offsets
+  int32_t* split_slot;// [batch*nkt*Hkv + 1] (MFMA path) accumulator slot of each split key tile
+  int max_split;     // (MFMA path) slots of dk_acc / dv_acc
   int32_t* queues;   // [8] work counters of the key-major pass
 };
 
@@ -87,6 +89,10 @@ hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const
                            hipStream_t st);
 bool bwd_mfma_supported(const Prefill& p);
 int bwd_num_tiles(const Prefill& p);        // key tiles of the key-major pass
+// Upper bound on the key tiles whose work is split over several work items
+// (they accumulate dK/dV in float32 slots); a tile beyond the bound is not
+// split (correct, only less balanced).
+int bwd_max_split_tiles(const Prefill& p);
 hipError_t launch_block_csr(const Prefill& p, const BwdWork& w, hipStream_t st);
 int block_csr_words(const Prefill& p);      // 32-bit words per reverse-list bit row
 int dsink_slabs(int total);                 // row slabs of the dsink reduction

@@ -95,7 +95,9 @@ size_t elem_size(int dtype) { return dtype == SINK_ATTN_F32 ? 4 : 2; }
 
 // Backward workspace layout (each section 256-byte aligned).
 struct BwdLayout {
-  size_t delta, lnew, terms, dsink_part, dq_acc, dk_acc, dv_acc, csr_off, csr_idx, csr_bits, plan, queues, total;
+  size_t delta, lnew, terms, dsink_part, dq_acc, dk_acc, dv_acc, csr_off, csr_idx, csr_bits, plan, split_slot,
+      queues, total;
+  int max_split;
 };
 
 BwdLayout bwd_layout(const sa::Prefill& p) {
@@ -109,14 +111,19 @@ BwdLayout bwd_layout(const sa::Prefill& p) {
   l.terms = off; off += round_up(rows * 4);
   l.dsink_part = off; off += round_up(static_cast<size_t>(sa::dsink_slabs(p.total)) * p.hq * 4);
   l.dq_acc = off;                                   // unused: dQ is stored directly
-  l.dk_acc = off; off += round_up(kv * 4);          // generic path; split key tiles
-  l.dv_acc = off; off += round_up(kv * 4);
+  // float32 dK/dV: every row on the generic path, split key tiles only on the
+  // matrix-core path (64 rows of D per tile)
+  l.max_split = mfma ? sa::bwd_max_split_tiles(p) : 0;
+  const size_t acc = mfma ? static_cast<size_t>(l.max_split) * 64 * p.d : kv;
+  l.dk_acc = off; off += round_up(acc * 4);
+  l.dv_acc = off; off += round_up(acc * 4);
   const size_t nl = p.blocks ? static_cast<size_t>(p.nqb) * p.hkv : 0;
   l.csr_off = off; off += (p.blocks && mfma) ? round_up((nl + 1) * 4) : 0;
   l.csr_idx = off; off += (p.blocks && mfma) ? round_up(nl * p.max_blocks * 4) : 0;
   l.csr_bits = off;
   off += (p.blocks && mfma) ? round_up(nl * static_cast<size_t>(sa::block_csr_words(p)) * 4) : 0;
   l.plan = off; off += mfma ? round_up((static_cast<size_t>(sa::bwd_num_tiles(p)) + 1) * 4) : 0;
+  l.split_slot = off; off += mfma ? round_up((static_cast<size_t>(sa::bwd_num_tiles(p)) + 1) * 4) : 0;
   l.queues = off; off += mfma ? round_up(8 * 4) : 0;
   l.total = off;
   return l;
@@ -466,6 +473,8 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     w.csr_idx = reinterpret_cast<int32_t*>(base + lay.csr_idx);
     w.csr_bits = reinterpret_cast<uint32_t*>(base + lay.csr_bits);
     w.plan = reinterpret_cast<int32_t*>(base + lay.plan);
+    w.split_slot = reinterpret_cast<int32_t*>(base + lay.split_slot);
+    w.max_split = lay.max_split;
     w.queues = reinterpret_cast<int32_t*>(base + lay.queues);
     const bool mfma = sa::bwd_mfma_supported(p);
     hipError_t e;
