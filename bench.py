@@ -100,46 +100,49 @@ def _dev_bf16(t, torch):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock on a host thread: the firmware metrics
-    table's current clock of each XCD (amdsmi), averaged over the XCDs, every
-    5 ms from the start of a leg's warm-up to the end of its timed region.
-    The figure reported is the median over the last 150 ms (the warm-up
-    brought the clocks to their loaded level); None where the interface is
-    not available."""
-
-    WINDOW_S = 0.15
+    """Samples the GPU's graphics clock on a host thread every 5 ms while a
+    leg's timed region runs: the current level of the kernel driver's
+    pp_dpm_sclk file, which follows the live clock (the firmware metrics
+    table that amdsmi reads refreshes only about once a second).  Reports
+    the median and range in MHz, or None where the file is not readable."""
 
     def __init__(self):
-        self.handle = None
+        import glob
+        self.path = None
         self.samples = []
         self._stop = None
         self._thread = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self.amdsmi = amdsmi
-            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read()
-        except Exception:  # noqa: BLE001 - no clock reading, nothing else changes
-            self.handle = None
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                if self._parse(open(f).read()) is not None:
+                    self.path = f
+                    break
+            except OSError:
+                continue
 
-    def _read(self):
-        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
-        clks = [float(c) for c in m["current_gfxclks"] if str(c) not in ("N/A", "65535")]
-        return sum(clks) / len(clks)
+    @staticmethod
+    def _parse(text):
+        for line in text.splitlines():
+            if line.rstrip().endswith("*"):
+                mhz = line.split(":", 1)[1].strip().rstrip("*").strip().lower().replace("mhz", "")
+                return float(mhz)
+        return None
 
     def start(self):
         import threading
         self.samples = []
-        if self.handle is None:
+        if self.path is None:
             return
         self._stop = threading.Event()
 
         def poll():
             while not self._stop.is_set():
                 try:
-                    self.samples.append((time.perf_counter(), self._read()))
-                except Exception:  # noqa: BLE001
+                    with open(self.path) as fh:
+                        v = self._parse(fh.read())
+                    if v is not None:
+                        self.samples.append(v)
+                except OSError:
                     return
                 self._stop.wait(0.005)
 
@@ -153,8 +156,7 @@ class ClockSampler:
             self._thread = None
         if not self.samples:
             return None
-        t_end = self.samples[-1][0]
-        x = np.array([c for t, c in self.samples if t >= t_end - self.WINDOW_S])
+        x = np.array(self.samples)
         return {"median_mhz": round(float(np.median(x)), 1), "min_mhz": round(float(x.min()), 1),
                 "max_mhz": round(float(x.max()), 1), "samples": int(x.size)}
 
@@ -163,13 +165,14 @@ class Timer:
     """HIP events on the current stream (the one the binding enqueues on).
 
     Warm-up runs at least `warmup` steps and at least MIN_WARM_MS of GPU time
-    (a GPU coming out of idle runs its first tens of milliseconds at lower
-    clocks).  The timed region records one event between consecutive steps,
+    (a GPU coming out of idle raises its clock over about half a second of
+    load: measured 355 MHz idle, ~1940 MHz after 250 ms, ~2070 MHz after
+    450 ms of back-to-back forwards).  The timed region records one event between consecutive steps,
     with no host synchronisation inside it, so the stream stays busy and every
     step's time is its own; the median step is reported, the mean and range
     beside it."""
 
-    MIN_WARM_MS = 250.0
+    MIN_WARM_MS = 600.0
 
     def __init__(self, torch, clock=None):
         self.torch = torch
@@ -214,16 +217,16 @@ class Timer:
 
     def run(self, fn, steps, warmup, per_step=1):
         """Returns a dict: median, mean, min, max ms per call; wall ms per
-        step; warm-up steps run; the clock near the timed region.  A step of
+        step; warm-up steps run; the clock during the timed region.  A step of
         `fn` holds `per_step` calls (a graph replay of several launches)."""
         return self.run_many([fn], steps, warmup, per_step)[0]
 
     def run_many(self, fns, steps, warmup, per_step=1):
-        if self.clock is not None:
-            self.clock.start()
         n_warm = 0
         for fn in fns:
             n_warm = max(n_warm, self.warm(fn, warmup))
+        if self.clock is not None:
+            self.clock.start()
         per, wall = self.timed(fns, steps)
         clk = self.clock.stop() if self.clock is not None else None
         out = []
@@ -673,9 +676,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20,
-                    help="untimed steps first (at least this many, and at least 250 ms of GPU "
-                         "time: the GPU reaches its steady clocks only after tens of "
-                         "milliseconds of load)")
+                    help="untimed steps first (at least this many, and at least 600 ms of GPU "
+                         "time: the GPU raises its clock over about half a second of load)")
+    ap.add_argument("--min-warm-ms", type=float, default=Timer.MIN_WARM_MS,
+                    help="GPU time every leg's warm-up runs at least (profiler runs pass 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", choices=("all", "headline", "decode", "streaming", "blocks", "gated",
                                        "decode_q8", "prefill_cache", "peaks"),
@@ -693,6 +697,8 @@ def main():
     import torch
     import streamingllm_sink_attn_amd as sa
     from streamingllm_sink_attn_amd import workloads as W
+
+    Timer.MIN_WARM_MS = args.min_warm_ms
 
     sa.lib()
     if args.calibrate_copy:
