@@ -250,8 +250,15 @@ int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
  *   o             output bfloat16 [B, chunk, num_q_heads, D]; lse, s float32
  *                 [B, chunk, num_q_heads] as sink_attn_fwd (s may be NULL).
  *   workspace     sink_attn_kvcache_prefill_workspace_size bytes, 256-byte
- *                 aligned (the per-sequence packed samples: B x (n_sink +
- *                 window + chunk) rows of K, V, Q and O).
+ *                 aligned: the bounds of the per-sequence samples, and for
+ *                 the 8-bit cache or head_dim other than 128 the samples
+ *                 themselves (B x (n_sink + window + chunk) packed rows of K
+ *                 and V; of Q and O too for head_dim other than 128).  With
+ *                 the bfloat16 cache and head_dim 128 the keys and values
+ *                 are read in place from the cache and k_new / v_new, and
+ *                 the workspace holds only copies of the at most three
+ *                 64-row key tiles per sequence that span a seam (first
+ *                 tokens to ring, the ring's wrap, ring to chunk).
  * The cache is read, not written: append the chunk afterwards with
  * sink_attn_kvcache_append and the same n_seen (appending first could evict
  * ring tokens the chunk's earlier rows still see).

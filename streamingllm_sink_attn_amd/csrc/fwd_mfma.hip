@@ -38,10 +38,18 @@
 //     Key 0 of a sample is element (M-tile 0, i 0) of the lanes of half 0 in
 //     key tile 0, so its probability is kept beside the row sum (rescaled
 //     with it) and the epilogue writes (l - l_0) / l.
+//   * Keys and values in place (instantiation CACHE, chunked prefill against
+//     a rolling cache): a sample's key rows are the stream's kept first
+//     tokens, its ring tokens oldest first, then the new chunk.  A 64-row
+//     tile inside one contiguous run (first tokens, ring rows on one side of
+//     the wrap, chunk rows) loads as any tile, from a per-tile base in the
+//     cache or the chunk; the at most three tiles of a stream that hold a
+//     seam load from copies staged beforehand (stream_rows.cuh).
 #include <cstdlib>
 #include <type_traits>
 
 #include "qmajor.cuh"
+#include "stream_rows.cuh"
 
 namespace sa {
 namespace fwd128 {
@@ -71,7 +79,7 @@ __device__ __forceinline__ u32x2 lds_tr(const lds_char* base, int byte_off) {
                                        (__attribute__((address_space(3))) i16x4*)(base + byte_off)));
 }
 
-template <bool GATE>
+template <bool GATE, bool CACHE>
 __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
                                                           const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
@@ -79,7 +87,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
                                                           uint16_t* __restrict__ O,
                                                           float* __restrict__ lse_out,
                                                           float* __restrict__ s_out,
-                                                          float* __restrict__ gate_out) {
+                                                          float* __restrict__ gate_out, CacheKv ckv) {
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][TILE];
   __shared__ uint32_t bitmap[BITMAP_LDS_WORDS];
@@ -160,18 +168,47 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   float l0 = 0.f;                                    // GATE: P of the sample's first key
 
   const int kvs = p.hkv * D;
-  const uint16_t* Kg = K + static_cast<size_t>(t0) * kvs + g * D;
-  const uint16_t* Vg = V + static_cast<size_t>(t0) * kvs + g * D;
+  const uint16_t* Kg = CACHE ? nullptr : K + static_cast<size_t>(t0) * kvs + g * D;
+  const uint16_t* Vg = CACHE ? nullptr : V + static_cast<size_t>(t0) * kvs + g * D;
   DmaTiles<FNW> ld;
   ld.init(w, lane, kvs);
   const uint32_t kbuf0 = lds_address(&kbuf[0][0]), vbuf0 = lds_address(&vbuf[0][0]);
+  // CACHE: sample 2 sb is stream sb's keys (first tokens, ring, chunk); each
+  // key tile is read from one base (wave-uniform): a contiguous run of the
+  // cache or of the chunk, or the stream's staged copy of a seam tile.
+  int c_sb = 0;
+  StreamRows sr{};
+  if constexpr (CACHE) {
+    c_sb = wc.b >> 1;
+    sr.init(ckv.n_seen[c_sb], ckv.n_sink, ckv.window, ckv.chunk);
+  }
+  auto cache_base = [&](const uint16_t* cbase, const uint16_t* nbase, const uint16_t* sbase,
+                        int kt) -> const uint16_t* {
+    int row;
+    const int kind = sr.tile_kind(kt, &row);
+    size_t r;
+    const uint16_t* base;
+    if (kind == 0) {
+      base = nbase;
+      r = static_cast<size_t>(c_sb) * ckv.chunk + row;
+    } else if (kind == 1) {
+      base = cbase;
+      r = static_cast<size_t>(c_sb) * ckv.slots + row;
+    } else {
+      base = sbase;
+      r = (static_cast<size_t>(c_sb) * kSeamSlots + sr.seam_slot(kt)) * kSeamRows;
+    }
+    return base + r * kvs + g * D;
+  };
   auto issue_k = [&](int kt, int st) {
     const int k0 = kt * BN;
-    ld.load(Kg + static_cast<size_t>(k0) * kvs, L - k0, kbuf0 + static_cast<uint32_t>(st * TILE * 2));
+    const uint32_t lds = kbuf0 + static_cast<uint32_t>(st * TILE * 2);
+    ld.load(CACHE ? cache_base(ckv.k, ckv.kn, ckv.sk, kt) : Kg + static_cast<size_t>(k0) * kvs, L - k0, lds);
   };
   auto issue_v = [&](int kt, int st) {
     const int k0 = kt * BN;
-    ld.load(Vg + static_cast<size_t>(k0) * kvs, L - k0, vbuf0 + static_cast<uint32_t>(st * TILE * 2));
+    const uint32_t lds = vbuf0 + static_cast<uint32_t>(st * TILE * 2);
+    ld.load(CACHE ? cache_base(ckv.v, ckv.vn, ckv.sv, kt) : Vg + static_cast<size_t>(k0) * kvs, L - k0, lds);
   };
   auto tile_class = [&](int kt) { return kt >= 0 ? wave_tile_class(p, sc, p0, wq0, wq1, kt) : 0; };
 
@@ -442,10 +479,22 @@ hipError_t launch_fwd_mfma(const Prefill& p, const void* q, const void* k, const
   const qm::Geo geo = qm::make_geo(p, fwd128::FNW, fwd128::FQW);
   const long long grid = static_cast<long long>(geo.nptiles) * p.batch * geo.Z;
   if (grid <= 0) return hipSuccess;
-  auto kern = gate0 ? fwd128::fwd_kernel<true> : fwd128::fwd_kernel<false>;
+  auto kern = gate0 ? fwd128::fwd_kernel<true, false> : fwd128::fwd_kernel<false, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(64 * fwd128::FNW), 0, st, p, geo,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, s, gate0);
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, s, gate0, CacheKv{});
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma_cache(const Prefill& p, const CacheKv& ckv, const void* q, void* o, float* lse,
+                                 float* s, hipStream_t st) {
+  if (p.total == 0 || p.batch == 0) return hipSuccess;
+  const qm::Geo geo = qm::make_geo(p, fwd128::FNW, fwd128::FQW);
+  const long long grid = static_cast<long long>(geo.nptiles) * p.batch * geo.Z;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd128::fwd_kernel<false, true>), dim3(static_cast<unsigned>(grid)), dim3(64 * fwd128::FNW),
+                     0, st, p, geo, static_cast<const uint16_t*>(q), nullptr, nullptr, static_cast<uint16_t*>(o),
+                     lse, s, nullptr, ckv);
   return hipGetLastError();
 }
 

@@ -70,6 +70,25 @@ struct KvCache {
   float* win_v_scale;
 };
 
+// Keys and values of a chunked prefill read in place (bf16 cache, D = 128):
+// sample 2b of the forward launch is stream b's keys in position order
+// [kept first tokens | ring tokens, oldest first | chunk]; sample 2b + 1 is
+// padding with no query row.  Key tiles inside one run are read from the
+// cache or the chunk; the few tiles holding a seam (see stream_rows.cuh)
+// are copied first to the staging tiles sk / sv.
+constexpr int kSeamSlots = 3;
+constexpr int kSeamRows = 64;
+struct CacheKv {
+  const uint16_t* k;          // bf16 [B, slots, Hkv, D]
+  const uint16_t* v;
+  const uint16_t* kn;         // bf16 [B, chunk, Hkv, D]
+  const uint16_t* vn;
+  uint16_t* sk;               // bf16 [B, 3, 64, Hkv, D] staged seam tiles
+  uint16_t* sv;
+  const int32_t* n_seen;      // [B] tokens each stream held before the chunk
+  int batch, hkv, slots, n_sink, window, chunk;
+};
+
 // ---- launchers (each returns hipGetLastError() of its launches) ----
 // gate0: float32 [T, Hq] first-token gate, or nullptr (not computed).
 hipError_t launch_fwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
@@ -77,6 +96,10 @@ hipError_t launch_fwd_generic(const Prefill& p, const void* q, const void* k, co
 hipError_t launch_fwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
                            void* o, float* lse, float* s, float* gate0, hipStream_t st);
 bool fwd_mfma_supported(const Prefill& p);
+// The matrix-core forward with K and V read in place from a rolling cache and
+// a chunk (p describes the 2B samples; p.qstart and p.qo_base are set).
+hipError_t launch_fwd_mfma_cache(const Prefill& p, const CacheKv& ckv, const void* q, void* o, float* lse,
+                                 float* s, hipStream_t st);
 
 hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* lse,
                                  const void* dout, const BwdWork& w, bool zero_dq,
@@ -122,6 +145,11 @@ hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const 
                                          const void* v_new, int chunk, int hq, const int32_t* n_seen,
                                          int lmax, void* kp, void* vp, void* qp, int32_t* cu,
                                          int32_t* qstart, int32_t* qo_base, hipStream_t st);
+// A chunked prefill whose keys are read in place: the sample bounds cu
+// (2B + 1), qstart and qo_base (2B each), as the gather writes them, and the
+// staged seam tiles of ckv.
+hipError_t launch_kvcache_prefill_plan(const CacheKv& ckv, int lmax, int32_t* cu, int32_t* qstart,
+                                       int32_t* qo_base, hipStream_t st);
 hipError_t launch_kvcache_prefill_scatter(const KvCache& c, int chunk, int hq, const int32_t* n_seen,
                                           int lmax, const void* op, const float* lsep, const float* sp,
                                           void* o, float* lse, float* s, hipStream_t st);

@@ -13,6 +13,7 @@
 // KV head) row: scale = amax / 448, code = e4m3(x * (448 / amax)), rounded to
 // nearest even by the hardware conversion; a zero row gets scale 0.
 #include "common.cuh"
+#include "stream_rows.cuh"
 
 namespace sa {
 namespace kvc {
@@ -122,6 +123,50 @@ __device__ __forceinline__ Seg segment(const KvCache& c, int p0, int chunk) {
   s.nw = min(max(p0 - c.n_sink, 0), c.window);
   s.L = s.ns + s.nw + chunk;
   return s;
+}
+
+// Chunked prefill with keys read in place.  Block (b, i, part): seam kind
+// i of stream b (see stream_rows.cuh), rows 4 part .. 4 part + 3 of its
+// tile, copied to staging slot i when that kind owns the tile; block
+// (b, 0, 0) also writes the bounds of the stream's sample (2b: first tokens,
+// ring, chunk) and of the padding sample after it (2b + 1, no query rows),
+// and where the chunk rows sit in the caller's [B, chunk] Q and outputs.
+constexpr int kStageParts = sa::kSeamRows / 4;
+__global__ __launch_bounds__(256) void prefill_plan_kernel(CacheKv ckv, int lmax, int32_t* __restrict__ cu,
+                                                           int32_t* __restrict__ qstart,
+                                                           int32_t* __restrict__ qo_base) {
+  const int part = blockIdx.x % kStageParts;
+  const int i = (blockIdx.x / kStageParts) % sa::kSeamSlots;
+  const int b = blockIdx.x / (kStageParts * sa::kSeamSlots);
+  sa::StreamRows sr;
+  sr.init(ckv.n_seen[b], ckv.n_sink, ckv.window, ckv.chunk);
+  if (i == 0 && part == 0 && threadIdx.x == 0) {
+    cu[2 * b] = b * lmax;
+    cu[2 * b + 1] = b * lmax + sr.L;
+    qstart[2 * b] = sr.L - ckv.chunk;
+    qstart[2 * b + 1] = lmax - sr.L;
+    qo_base[2 * b] = b * ckv.chunk - (sr.L - ckv.chunk);
+    qo_base[2 * b + 1] = 0;
+    if (b == ckv.batch - 1) cu[2 * ckv.batch] = ckv.batch * lmax;
+  }
+  const int kt = sr.seam_tile(i);
+  int unused;
+  if (kt < 0 || sr.tile_kind(kt, &unused) != 2 || sr.seam_slot(kt) != i) return;
+  const int kvs = ckv.hkv * 128;
+  const int pieces = kvs / 8;                         // 16-byte pieces of a row
+  const size_t stage0 = (static_cast<size_t>(b) * sa::kSeamSlots + i) * sa::kSeamRows;
+  for (int e = threadIdx.x; e < 4 * pieces; e += blockDim.x) {
+    const int rr = 4 * part + e / pieces;             // row inside the tile
+    const int r = kt * sa::kSeamRows + rr;
+    if (r >= sr.L) break;                             // rows beyond the stream: never read
+    int row;
+    const bool in_cache = sr.source(r, &row);
+    const size_t src = (in_cache ? static_cast<size_t>(b) * ckv.slots + row
+                                 : static_cast<size_t>(b) * ckv.chunk + row) * kvs + 8 * (e % pieces);
+    const size_t dst = (stage0 + rr) * kvs + 8 * (e % pieces);
+    *reinterpret_cast<u32x4*>(ckv.sk + dst) = *reinterpret_cast<const u32x4*>((in_cache ? ckv.k : ckv.kn) + src);
+    *reinterpret_cast<u32x4*>(ckv.sv + dst) = *reinterpret_cast<const u32x4*>((in_cache ? ckv.v : ckv.vn) + src);
+  }
 }
 
 // 16 lanes per (sequence b, segment row i, KV head g): the K and V row of the
@@ -276,6 +321,15 @@ hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const 
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), chunk, hq, n_seen, lmax, static_cast<uint16_t*>(kp),
                      static_cast<uint16_t*>(vp), static_cast<uint16_t*>(qp), cu, qstart, qo_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvcache_prefill_plan(const CacheKv& ckv, int lmax, int32_t* cu, int32_t* qstart,
+                                       int32_t* qo_base, hipStream_t st) {
+  if (ckv.batch == 0) return hipSuccess;
+  const long long grid = static_cast<long long>(ckv.batch) * sa::kSeamSlots * kvc::kStageParts;
+  hipLaunchKernelGGL(kvc::prefill_plan_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, ckv, lmax,
+                     cu, qstart, qo_base);
   return hipGetLastError();
 }
 

@@ -577,20 +577,24 @@ int sink_attn_kvcache_decode(const sink_attn_kvcache_desc* cache, const void* q,
 // Chunked prefill: workspace sections of the packed per-sequence samples.
 // With head_dim 128 the matrix-core forward reads Q and writes the outputs in
 // the caller's [B, chunk] layout (direct); otherwise the generic forward works
-// on packed Q / O copies.
+// on packed Q / O copies.  With the bfloat16 cache as well (inplace) it also
+// reads K and V straight from the cache and the chunk: kp / vp then hold only
+// the staged seam tiles, 3 x 64 rows per stream.
 struct PrefillLayout {
   size_t cu, qstart, qo_base, kp, vp, qp, op, lsep, sp, total;
   long long lmax;
-  bool direct;
+  bool direct, inplace;
 };
 
 PrefillLayout kvcache_prefill_layout(const sink_attn_kvcache_desc* c, int32_t chunk, int32_t hq) {
   PrefillLayout l{};
   l.lmax = static_cast<long long>(c->n_sink) + c->window + chunk;
   l.direct = c->head_dim == 128;
-  const size_t rows = static_cast<size_t>(c->batch) * static_cast<size_t>(l.lmax);
+  l.inplace = l.direct && !c->quantized;
+  const size_t rows = l.inplace ? static_cast<size_t>(c->batch) * sa::kSeamSlots * sa::kSeamRows
+                                : static_cast<size_t>(c->batch) * static_cast<size_t>(l.lmax);
   const size_t D = static_cast<size_t>(c->head_dim);
-  const size_t qrows = l.direct ? 0 : rows;
+  const size_t qrows = l.direct ? 0 : static_cast<size_t>(c->batch) * static_cast<size_t>(l.lmax);
   size_t off = 0;
   l.cu = off; off += round_up((2 * static_cast<size_t>(c->batch) + 1) * 4);
   l.qstart = off; off += round_up(2 * static_cast<size_t>(c->batch) * 4);
@@ -667,9 +671,25 @@ int sink_attn_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lmax = static_cast<int>(l.lmax);
     int32_t* qo_base = l.direct ? reinterpret_cast<int32_t*>(ws + l.qo_base) : nullptr;
-    hipError_t e = sa::launch_kvcache_prefill_gather(kc, q, k_new, v_new, chunk, num_q_heads, n_seen, lmax,
-                                                     ws + l.kp, ws + l.vp, l.direct ? nullptr : ws + l.qp,
-                                                     cu, qstart, qo_base, st);
+    sa::CacheKv ckv;
+    ckv.k = static_cast<const uint16_t*>(cache->k);
+    ckv.v = static_cast<const uint16_t*>(cache->v);
+    ckv.kn = static_cast<const uint16_t*>(k_new);
+    ckv.vn = static_cast<const uint16_t*>(v_new);
+    ckv.sk = reinterpret_cast<uint16_t*>(ws + l.kp);
+    ckv.sv = reinterpret_cast<uint16_t*>(ws + l.vp);
+    ckv.n_seen = n_seen;
+    ckv.batch = cache->batch;
+    ckv.hkv = cache->num_kv_heads;
+    ckv.slots = cache->n_sink + cache->window;
+    ckv.n_sink = cache->n_sink;
+    ckv.window = cache->window;
+    ckv.chunk = chunk;
+    hipError_t e = l.inplace
+                       ? sa::launch_kvcache_prefill_plan(ckv, lmax, cu, qstart, qo_base, st)
+                       : sa::launch_kvcache_prefill_gather(kc, q, k_new, v_new, chunk, num_q_heads, n_seen, lmax,
+                                                           ws + l.kp, ws + l.vp, l.direct ? nullptr : ws + l.qp,
+                                                           cu, qstart, qo_base, st);
     if (e == hipSuccess) {
       sa::Prefill p;
       p.cu = cu;
@@ -691,7 +711,8 @@ int sink_attn_kvcache_prefill(const sink_attn_kvcache_desc* cache, const void* q
       p.qo_base = qo_base;
       if (l.direct != sa::fwd_mfma_supported(p))
         return fail(SINK_ATTN_HIP_ERROR, "internal: chunked prefill path mismatch");
-      e = l.direct ? sa::launch_fwd_mfma(p, q, ws + l.kp, ws + l.vp, o, lse, s, nullptr, st)
+      e = l.inplace  ? sa::launch_fwd_mfma_cache(p, ckv, q, o, lse, s, st)
+          : l.direct ? sa::launch_fwd_mfma(p, q, ws + l.kp, ws + l.vp, o, lse, s, nullptr, st)
                    : sa::launch_fwd_generic(p, ws + l.qp, ws + l.kp, ws + l.vp, ws + l.op, lsep, sp, nullptr, st);
     }
     if (e == hipSuccess && !l.direct)

@@ -266,15 +266,21 @@ def test_check_kvcache_prefill():
     assert pre(_kdesc(), q=FAKE + 4) == B.INVALID_ARGUMENT                  # misaligned
     assert pre(_kdesc(), s=FAKE) == B.OK
     assert pre(_kdesc(head_dim=64, **_Q8)) == B.UNSUPPORTED
-    for hd in (128, 64):
-        d = _kdesc(head_dim=hd)
+    for hd, quant in ((128, False), (64, False), (128, True)):
+        d = _kdesc(head_dim=hd, **(_Q8 if quant else {}))
         need = L.sink_attn_kvcache_prefill_workspace_size(ctypes.byref(d), 16, 8)
         rows = d.batch * (d.n_sink + d.window + 16)
-        # packed K, V (Hkv heads) in bf16; head_dim 128 reads Q and writes the
-        # outputs in place, other sizes also pack Q, O (bf16) and LSE, s (float32)
-        kv = 2 * d.num_kv_heads * hd * 2
+        kv = 2 * d.num_kv_heads * hd * 2                 # a K and a V row of Hkv heads, bf16
         qo = 0 if hd == 128 else 2 * 8 * hd * 2 + 2 * 8 * 4
-        assert rows * (kv + qo) <= need <= rows * (kv + qo) + 16 * 256
+        if hd == 128 and not quant:
+            # the bf16 cache with head_dim 128 is read in place: only the
+            # three staged 64-row seam tiles of each stream
+            staged = d.batch * 3 * 64 * kv
+            assert staged <= need <= staged + 16 * 256
+        else:
+            # packed K, V; for head_dim other than 128 also packed Q, O (bf16)
+            # and LSE, s (float32)
+            assert rows * (kv + qo) <= need <= rows * (kv + qo) + 16 * 256
         assert pre(d, ws=need - 1) == B.WORKSPACE_TOO_SMALL
     assert pre(_kdesc(batch=60000, window=1 << 20)) == B.UNSUPPORTED         # packed rows past 2^31
 

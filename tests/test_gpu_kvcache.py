@@ -231,6 +231,19 @@ def test_prefill_over_cache(quantized, n_sink, window, chunks, start):
     _prefill_stream(rng, 3, 8, 2, 128, n_sink, window, quantized, chunks, start)
 
 
+@pytest.mark.parametrize("n_sink,window,chunks,start", [(70, 200, [150, 70, 64, 300], [0, 77, 500]),
+                                                        (0, 256, [64, 200, 129, 511], [0, 3, 1000]),
+                                                        (4, 130, [64, 1, 127, 130], [2, 66, 131])])
+def test_prefill_over_cache_tiles_in_place(n_sink, window, chunks, start):
+    """bf16 cache, D = 128: key tiles read from the cache and the chunk where
+    they lie (first tokens over more than one tile, ring runs before and
+    after the wrap, chunk runs) and seam tiles staged, at several ring
+    offsets per stream."""
+    print(f"[case] kvcache prefill in place {n_sink} {window} {chunks} {start}", flush=True)
+    rng = np.random.default_rng(26)
+    _prefill_stream(rng, 3, 8, 2, 128, n_sink, window, False, chunks, start)
+
+
 @pytest.mark.parametrize("quantized", [False, True])
 def test_prefill_over_cache_three_heads_per_group(quantized):
     """3 query heads per KV head (one head per workgroup, 256-row position
