@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   // S^T of a tile from K buffer ST.  The two 32-key halves alternate (two
   // independent accumulation chains) and every K fragment is read two MFMAs
   // ahead, in an order the scheduling barriers keep.
-  auto scores = [&](auto ST, f32x16 (&s)[2]) {
+  auto scores = [&](auto ST, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const lds_char* kb = (const lds_char*)(kbuf[decltype(ST)::value]);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -237,13 +237,16 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   // element.  The pair is visible iff dk <= a (causal) and, with a window,
   // dk > wb (inside the window) or dk < cs (a kept first token), with a, wb,
   // cs per lane: one or two compares and a select per element.
-  auto mask = [&](int kt, f32x16 (&s)[2]) {
+  auto mask = [&](int kt, f32x16 (&s)[2]) __attribute__((always_inline)) {
     const int kb = kt * BN + 4 * gq;
     const int a = qi - kb;
     // a window longer than qi + 1 keys, or none, covers the same keys as
     // qi + 1 (all causal keys): visible iff a - wlen < dk <= a
     const int wlen = p.window > 0 ? min(p.window, qi + 1) : qi + 1;
-    const int wb = a - wlen;
+    // per element: dk + nb < span with nb = -wb - 1; nb is pinned here so
+    // the compiler does not hoist 32 per-element sums out of the loop
+    int nb = wlen - a - 1;
+    asm volatile("" : "+v"(nb));
     const uint32_t span = static_cast<uint32_t>(wlen);
     if (p.window <= 0 || kt * BN >= p.n_sink) {      // uniform: no kept token here
 #pragma unroll
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
-          s[mt][i] = static_cast<uint32_t>(dk - wb - 1) < span ? s[mt][i] : -kInf;
+          s[mt][i] = static_cast<uint32_t>(dk + nb) < span ? s[mt][i] : -kInf;
         }
     } else {
       const int cs = min(p.n_sink - kb, a + 1);      // kept first tokens: dk < cs
@@ -260,14 +263,14 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int dk = 32 * mt + 8 * (i >> 2) + (i & 3);
-          const bool vis = static_cast<uint32_t>(dk - wb - 1) < span || dk < cs;
+          const bool vis = static_cast<uint32_t>(dk + nb) < span || dk < cs;
           s[mt][i] = vis ? s[mt][i] : -kInf;
         }
     }
   };
   // Row max of a tile and the lazy rescale to a new base of O, l and the
   // not yet accumulated probabilities pend (which share the old base).
-  auto update_max = [&](const f32x16 (&s)[2], bool dead, bf16x8 (&pend)[4]) {
+  auto update_max = [&](const f32x16 (&s)[2], bool dead, bf16x8 (&pend)[4]) __attribute__((always_inline)) {
     float m0 = -kInf;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   };
   // P = 2^(c x - mb) in bf16 as four k-steps, l += sum P.  first: this is
   // key tile 0 (GATE keeps the first key's P).
-  auto probs = [&](f32x16 (&s)[2], float mb, bool first, bf16x8 (&pf)[4]) {
+  auto probs = [&](f32x16 (&s)[2], float mb, bool first, bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     float ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     for (int cc = 0; cc < 4; ++cc) pf[cc] = pack_kstep(s[cc >> 1], cc & 1);
   };
   // O^T += V^T P^T from V buffer ST.
-  auto pv = [&](auto ST, const bf16x8 (&pf)[4]) {
+  auto pv = [&](auto ST, const bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     const lds_char* vb = (const lds_char*)(vbuf[decltype(ST)::value]);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
   // return the exponent base c m for its P.  A tile this wavefront does not
   // see leaves the max alone and takes an infinite base, so its P is exactly
   // 0 and its scores need no rewrite.
-  auto finish_scores = [&](int kt, f32x16 (&s)[2], bf16x8 (&pend)[4]) {
+  auto finish_scores = [&](int kt, f32x16 (&s)[2], bf16x8 (&pend)[4]) __attribute__((always_inline)) {
     const int cls = tile_class(kt);
     if (cls == 2) mask(kt, s);
     update_max(s, cls == 0, pend);
@@ -340,51 +343,112 @@ __global__ __launch_bounds__(64 * FNW, 1) void fwd_kernel(Prefill p, Geo geo,
     return mb;
   };
 
+  // One pipeline step covers three tiles in schedule order, cur, nx, nx2:
+  // P of cur is in pf (bf16) with V of cur in V buffer k%2, the raw scores
+  // of nx are in s_nx, and K of nx2 is in K buffer k%2 (step k).  After the
+  // mask, max and (rare) rescale of nx, one straight-line block runs the 16
+  // score MFMAs of nx2 and the 16 O += V P MFMAs of cur with the
+  // exponentials of nx between them: a wavefront's vector ALU work issues
+  // while its own MFMAs execute.  K of the tile after nx2 goes to K buffer
+  // (k+1)%2 and V of nx to V buffer (k+1)%2, both freed by the step before,
+  // and are waited for at the step's end.  Steps run until cur is the last
+  // tile; scores of tiles past the end come from whatever their K buffer
+  // holds (always a loaded tile) and are discarded (P = 0).
   int t_cur = sc.next();
   if (t_cur >= 0) {
     int t_nx = sc.next();
+    int t_nx2 = sc.next();
     issue_k(t_cur, 0);
     issue_v(t_cur, 0);
-    // K buffer 1 always holds a real tile: the last step forms (and
-    // discards) the scores of a tile that does not exist from it.
     issue_k(t_nx >= 0 ? t_nx : t_cur, 1);
     wait_bar<0>();
-    bf16x8 pf[4];                                    // P of tile "cur" (bf16)
+    bf16x8 pf[4];                                    // P of cur (bf16), not yet in O
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) pf[cc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    f32x16 s_nx[2];                                  // raw scores of nx
     {
       f32x16 s0[2];
       scores(std::integral_constant<int, 0>{}, s0);
       const float mb = finish_scores(t_cur, s0, pf);
       probs(s0, mb, t_cur == 0, pf);
+      scores(std::integral_constant<int, 1>{}, s_nx);
     }
+    wait_bar<0>();                                   // K buffer 0 no longer read
+    if (t_nx2 >= 0) issue_k(t_nx2, 0);
     wait_bar<0>();
 
-    // One pipeline step: P of tile "cur" is in pf and its V in V buffer ST;
-    // K of "nx" is in K buffer ST^1.  K of the tile after next goes to K
-    // buffer ST and V of "nx" to V buffer ST^1.  O += V P of "cur" (matrix
-    // core) is interleaved with the exponentials of "nx" (vector ALU).  The
-    // last step has no tile "nx": it forms the scores of whatever K buffer
-    // ST^1 holds and discards them as a tile this wavefront does not see
-    // (P = 0), so every step runs the same code and O needs no merge.
-    auto step = [&](auto ST) {
+    // The block of step k (K buffer and V buffer ST = k%2): s_nn = scores of
+    // nx2, O += V P of cur, pn = P of nx.  Slot x: score MFMA x (M-tile
+    // x%2, k-step x/2), P V MFMA x (k-step x/4, dim tile x%4), exponentials
+    // of elements 2x, 2x+1 of nx; K fragments read two slots ahead, V^T
+    // fragments one slot ahead.
+    auto block = [&](auto ST, f32x16 (&sn)[2], f32x16 (&sx)[2], float mb, bool first,
+                     bf16x8 (&pn)[4]) __attribute__((always_inline)) {
       constexpr int st = decltype(ST)::value;
-      const int t_nx2 = sc.next();
-      if (t_nx2 >= 0) issue_k(t_nx2, st);
+      const lds_char* kb = (const lds_char*)(kbuf[st]);
+      const lds_char* vb = (const lds_char*)(vbuf[st]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sn[mt][i] = 0.f;
+      bf16x8 kf[3], vf[2];
+      kf[0] = lds_frag(kb, koff[0]);
+      kf[1] = lds_frag(kb, koff[0] + 8192);
+      auto vfrag = [&](int x) __attribute__((always_inline)) {
+        const int cc = x >> 2, dt = x & 3;
+        const u32x2 lo = lds_tr(vb, voa[dt] + cc * 4096);
+        const u32x2 hi = lds_tr(vb, vob[dt] + cc * 4096);
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      };
+      vf[0] = vfrag(0);
+      float ls = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        if (x + 2 < 16) kf[(x + 2) % 3] = lds_frag(kb, koff[(x + 2) >> 1] + ((x + 2) & 1) * 8192);
+        if (x + 1 < 16) vf[(x + 1) & 1] = vfrag(x + 1);
+        // each MFMA is followed by vector work that does not depend on it,
+        // which issues while it executes
+        auto expo = [&](int e) __attribute__((always_inline)) {
+          const int mt = (2 * x + e) >> 4, i = (2 * x + e) & 15;
+          const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[mt][i], c, -mb));
+          sx[mt][i] = ex;
+          ls += ex;
+          asm volatile("" : "+v"(ls));               // the row sum stays in its slot
+        };
+        sn[x & 1] = mfma32(kf[x % 3], qf[x >> 1], sn[x & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        expo(0);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[x & 3] = mfma32(vf[x & 1], pf[x >> 2], oacc[x & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        expo(1);
+        if ((x & 3) == 3) pn[x >> 2] = pack_kstep(sx[x >> 3], (x >> 2) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lsum += ls;
+      if constexpr (GATE) {
+        if (first) l0 += gq == 0 ? sx[0][0] : 0.f;   // uniform branch
+      }
+    };
+    auto step = [&](auto ST) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      const int t_nx3 = sc.next();
+      if (t_nx3 >= 0) issue_k(t_nx3, st ^ 1);
       if (t_nx >= 0) issue_v(t_nx, st ^ 1);
-      f32x16 s_nx[2];
-      scores(std::integral_constant<int, st ^ 1>{}, s_nx);
       const float mb = finish_scores(t_nx, s_nx, pf);
+      f32x16 s_nn[2];
       bf16x8 pn[4];
-      pv(std::integral_constant<int, st>{}, pf);
-      probs(s_nx, mb, t_nx == 0, pn);
+      block(ST, s_nn, s_nx, mb, t_nx == 0, pn);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) pf[cc] = pn[cc];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) s_nx[mt] = s_nn[mt];
       // This step's loads landed and no read of the buffers they refill next
       // step is in flight.
       wait_bar<0>();
       t_cur = t_nx;
       t_nx = t_nx2;
+      t_nx2 = t_nx3;
     };
     while (true) {                                   // t_cur is uniform over the workgroup
       step(std::integral_constant<int, 0>{});
