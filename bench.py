@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ('fwd_mfma.hip', 'qmajor.cuh', 'common.cuh', 'internal.h', 'stream_rows.cuh'),
-    "sha256": "3e994da5a5a7ede45ae08873487c59c83bde7279ebc077627528d1b4b8d0bb5f",
-    "read_bytes": 224648872,
-    "write_bytes": 142970546,
+    "sha256": "ea0296607e0efa8f8a9bac66d28df00e27defd2de4db5c5ae6d4156a361cf79f",
+    "read_bytes": 231041760,
+    "write_bytes": 142688087,
 }
 
 
