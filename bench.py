@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ('fwd_mfma.hip', 'qmajor.cuh', 'common.cuh', 'internal.h', 'stream_rows.cuh'),
-    "sha256": "ea0296607e0efa8f8a9bac66d28df00e27defd2de4db5c5ae6d4156a361cf79f",
+    "sha256": "e4ef8bd8c7e6e30bd925bd3ba42f55d3bcbd5276c81d15f9bcce3204204ba274",
     "read_bytes": 231041760,
     "write_bytes": 142688087,
 }
@@ -411,8 +411,45 @@ def measured_peaks(torch, sa, clock=None, steps=10):
                       "clock": r["clock"]}
     if r["clock"]:
         out["exp_f32"]["per_clk_per_cu"] = round(ne / (r["median"] * 1e-3) / (256 * r["clock"]["median_mhz"] * 1e6), 2)
+    out["probes"] = probes(torch, sa)
     MEASURED.update(out)
     return out
+
+
+def probes(torch, sa):
+    """Cycle counts (s_memtime per wavefront, one 8-wavefront workgroup per
+    CU) of the co-issue and LDS-rate probes of libsinkattn_peaks.so: 16
+    MFMAs and/or 32 FMAs per iteration in one wavefront or split over the
+    two wavefronts of a SIMD; 16 LDS reads per lane per iteration."""
+    import ctypes
+    P = sa.binding.peaks_lib()
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    grid, iters = 256, 2000
+    o = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(grid * 8, dtype=torch.int64, device="cuda")
+    res = {}
+    names = {0: "16 mfma", 1: "32 fma", 2: "16 mfma + 32 fma, one wavefront",
+             3: "16 mfma on wavefronts 0-3, 32 fma on 4-7 (same SIMDs)"}
+    for mode, name in names.items():
+        for _ in range(2):                             # the second launch is the measured one
+            assert P.sink_attn_peaks_coissue(mode, iters, ctypes.c_void_p(o.data_ptr()),
+                                             ctypes.c_void_p(cyc.data_ptr()), grid, st()) == 0
+        torch.cuda.synchronize()
+        c = cyc.view(grid, 8).double() / iters
+        if mode == 3:
+            res[name] = {"mfma_wave_cycles_per_iter": round(c[:, :4].mean().item(), 1),
+                         "fma_wave_cycles_per_iter": round(c[:, 4:].mean().item(), 1)}
+        else:
+            res[name] = {"cycles_per_iter": round(c.mean().item(), 1), "max": round(c.max().item(), 1)}
+    lo = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    for mode, (name, nb) in {0: ("ds_read_b128", 16), 1: ("ds_read_b64", 8), 2: ("ds_read_b64_tr_b16", 8)}.items():
+        for _ in range(2):
+            assert P.sink_attn_peaks_lds(mode, iters, ctypes.c_void_p(lo.data_ptr()),
+                                         ctypes.c_void_p(cyc.data_ptr()), grid, st()) == 0
+        torch.cuda.synchronize()
+        slowest = cyc.view(grid, 8).max().item()
+        res[name] = {"bytes_per_clk_per_cu": round(512 * iters * 16 * nb / slowest, 1)}
+    return res
 
 
 def bench_decode(torch, sa, W, steps, warmup, clock=None):

@@ -163,6 +163,8 @@ PEAKS_SIGS = {
     "sink_attn_peaks_read": (c_i32, [c_vp, ctypes.c_size_t, c_vp, c_i32, c_vp]),
     "sink_attn_peaks_mfma": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
     "sink_attn_peaks_exp": (c_i32, [c_i32, c_vp, c_i32, c_vp]),
+    "sink_attn_peaks_coissue": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_vp]),
+    "sink_attn_peaks_lds": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_i32, c_vp]),
 }
 
 

@@ -25,12 +25,14 @@
 //     registers plus one v_permlane32_swap between the lane halves.  The same
 //     registers, converted to bf16, are the B operand of O^T += V^T P^T; the
 //     V^T operand comes from the staged V tile by ds_read_b64_tr_b16.
-//   * Software pipeline: a step forms the scores of tile j+1 (K fragments
-//     read two MFMAs ahead), masks them and takes their row max, then runs
-//     O += V P of tile j on the matrix core interleaved with the
-//     exponentials of tile j+1 on the vector ALU; the two wavefronts of a
-//     SIMD overlap one another's phases.  K runs one tile ahead of V: K and
-//     V each have two LDS buffers.
+//   * Software pipeline over three tiles: a step masks the scores of tile
+//     j+1 and takes their row max, then runs one straight-line block of 16
+//     slots, each holding a score MFMA of tile j+2 (K fragments read two
+//     slots ahead), two exponentials of tile j+1 with their row sum, an
+//     O += V P MFMA of tile j and two more exponentials.  A wavefront's
+//     independent vector ALU work issues while its own MFMAs execute, so the
+//     exponentials no longer wait for the score MFMAs of their tile.  K runs
+//     two tiles ahead of V; K and V each have two LDS buffers.
 //   * Online softmax with lazy rescaling: the exponent base only moves when a
 //     row's max grows by more than 2^8 (P <= 256), which is exact because O
 //     and l always share the same base.

@@ -25,7 +25,7 @@ def test_peaks_library_exports_every_declared_symbol():
     text = open(os.path.join(ROOT, "include", "sink_attn_peaks.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(sink_attn_peaks_[a-z_]+)\s*\(", text)))
-    assert len(names) == 3
+    assert len(names) == 5
     lib = B.peaks_lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -35,6 +35,10 @@ def test_peaks_library_exports_every_declared_symbol():
     assert lib.sink_attn_peaks_read(FAKE, 15, FAKE, 1, None) == 1
     assert lib.sink_attn_peaks_mfma(0, FAKE, 1, None) == 1
     assert lib.sink_attn_peaks_exp(5, None, 1, None) == 1
+    assert lib.sink_attn_peaks_coissue(4, 10, FAKE, FAKE, 1, None) == 1      # no such mode
+    assert lib.sink_attn_peaks_coissue(0, 10, FAKE, None, 1, None) == 1
+    assert lib.sink_attn_peaks_lds(3, 10, FAKE, FAKE, 1, None) == 1
+    assert lib.sink_attn_peaks_lds(0, 0, FAKE, FAKE, 1, None) == 1
 
 
 def test_library_exports_every_declared_symbol():
