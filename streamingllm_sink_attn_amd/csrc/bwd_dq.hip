@@ -103,6 +103,34 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
     ld.load(Vg + static_cast<size_t>(k0) * kvs, L - k0, kv0 + static_cast<uint32_t>((2 * st + 1) * TILE * 2));
   };
 
+  // Per-lane LDS byte offsets of a staged tile, each family one base and an
+  // XOR (the swizzle only permutes the bits the index moves), so the loop
+  // holds three registers instead of twelve offsets: row fragment (row
+  // 32mt + l32, logical chunk gq*8 + ks) at (rf ^ (ks << 4)) + 8192 mt;
+  // transposed pair (rows 16cc + ra and +8, dims dt*32 + d) at
+  // (ta | tb) ^ (dt << 6), plus 4096 cc.
+  const int rf = l32 * 256 + (((gq * 8) ^ swz16(l32)) << 4);
+  int ta, tb;
+  {
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int r = l16 >> 2, q4 = l16 & 3;
+    const int c0 = 2 * (grp & 1) + (q4 >> 1), off = 8 * (q4 & 1);
+    const int ra = 4 * (grp >> 1) + r;
+    ta = ra * 256 + ((c0 ^ swz16(ra)) << 4) + off;
+    tb = (ra + 8) * 256 + ((c0 ^ swz16(ra + 8)) << 4) + off;
+  }
+  typedef __attribute__((address_space(3))) char lds_char;
+  auto frag = [&](const lds_char* t, int o) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(t + o));
+  };
+  auto tr_pair = [&](const lds_char* t, int oa, int ob) __attribute__((always_inline)) {
+    const u32x2 a = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(t + oa)));
+    const u32x2 b = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(t + ob)));
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+  };
+
   int kt = sc.next();
   if (kt >= 0) issue(kt, 0);
   wait_bar<0>();
@@ -113,19 +141,35 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
 
     const int cls = wave_tile_class(p, sc, p0, wq0, wq1, kt);
     if (cls != 0) {
-      const uint16_t* Ks = kv[stage][0];
-      const uint16_t* Vs = kv[stage][1];
+      const lds_char* Ks = (const lds_char*)(kv[stage][0]);
+      const lds_char* Vs = (const lds_char*)(kv[stage][1]);
       const int k0 = kt * BN;
-      // S^T = K Q^T and dP^T = V dO^T : M = keys (2 tiles), N = 32 queries
+      // S^T = K Q^T and dP^T = V dO^T : M = keys (2 tiles), N = 32 queries.
+      // Fragments are read two MFMA pairs ahead (order kept by the
+      // scheduling barriers), so LDS latency overlaps the matrix core.
       f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) { sacc[mt][i] = 0.f; pacc[mt][i] = 0.f; }
+      {
+        bf16x8 fk[3], fv[3];
+        auto roff = [&](int y) { return (rf ^ ((y & 7) << 4)) + (y >> 3) * 8192; };
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sacc[mt] = mfma32(row_frag(Ks, mt * 32 + l32, gq * 8 + ks), qf[ks], sacc[mt]);
-          pacc[mt] = mfma32(row_frag(Vs, mt * 32 + l32, gq * 8 + ks), dof[ks], pacc[mt]);
+        for (int y = 0; y < 2; ++y) {
+          fk[y] = frag(Ks, roff(y));
+          fv[y] = frag(Vs, roff(y));
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int mt = x >> 3, ks = x & 7;
+          if (x + 2 < 16) {
+            fk[(x + 2) % 3] = frag(Ks, roff(x + 2));
+            fv[(x + 2) % 3] = frag(Vs, roff(x + 2));
+          }
+          sacc[mt] = mfma32(fk[x % 3], qf[ks], sacc[mt]);
+          pacc[mt] = mfma32(fv[x % 3], dof[ks], pacc[mt]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // dS^T = P^T (dP^T - Delta); element i of lane (l32, gq) in M-tile mt is
@@ -170,7 +214,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(Prefill p, Geo geo,
       for (int cc = 0; cc < 4; ++cc) {
         const bf16x8 dsb = pack_kstep(pacc[cc >> 1], cc & 1);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dqacc[dt] = mfma32(tr_frag(Ks, 16 * cc, dt * 32, lane), dsb, dqacc[dt]);
+        for (int dt = 0; dt < 4; ++dt)
+          dqacc[dt] = mfma32(tr_pair(Ks, (ta ^ (dt << 6)) + cc * 4096, (tb ^ (dt << 6)) + cc * 4096), dsb, dqacc[dt]);
       }
     }
     // The next tile landed and no read of this stage is in flight when it is
