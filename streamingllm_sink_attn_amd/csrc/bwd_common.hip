@@ -30,8 +30,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(Prefill p, const vo
     float acc = 0.f;
     for (int c = sub; c < nchunks; c += 16) {
       const size_t off = row * D + static_cast<size_t>(c) * kPerChunk;
-      u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const T*>(o) + off);
-      u32x4 dv = *reinterpret_cast<const u32x4*>(static_cast<const T*>(dout) + off);
+      // read once here: non-temporal, so the stream does not displace the
+      // tiles the backward kernels reuse from the caches
+      u32x4 ov = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(o) + off));
+      u32x4 dv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(dout) + off));
       if constexpr (sizeof(T) == 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc += __uint_as_float(ov[e]) * __uint_as_float(dv[e]);

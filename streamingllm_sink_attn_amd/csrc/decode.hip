@@ -84,6 +84,16 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                fp8x2_to_bf16x2(w1, true)};
 }
 
+// 16-byte cache load.  The bfloat16 cache streams through once per call:
+// non-temporal loads keep it from displacing other data in the caches and
+// measured faster; for the 8-bit ring, whose 128-byte rows each lane group
+// reads in pieces, they measured slower, so Q8 keeps ordinary loads.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+
 // First of the 8 dims that quarter gq holds at k-step ks.  bf16 cache: dims
 // ks*32 + gq*8, so the four quarters of a slot read 64 contiguous bytes per
 // k-step.  8-bit cache: (ks/2)*64 + gq*16 + (ks%2)*8, so one 16-byte load
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
       else slot = slot < p.slots ? slot : p.slots - 1;
       const uint16_t* src = Kb + static_cast<size_t>(slot) * row_stride;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = *reinterpret_cast<const u32x4*>(src + kdim<Q8>(ks, gq));
+      for (int ks = 0; ks < 4; ++ks) dst[mt][ks] = load16<!Q8>(src + kdim<Q8>(ks, gq));
     }
   };
   auto load_v = [&](int cs) {
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
       int slot = cs + (lane >> 4) + 4 * i;
       if constexpr (Q8) slot = min(slot, sink_last);
       else slot = slot < p.slots ? slot : p.slots - 1;
-      vr[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<size_t>(slot) * row_stride + l16 * 8);
+      vr[i] = load16<!Q8>(Vb + static_cast<size_t>(slot) * row_stride + l16 * 8);
     }
   };
   auto store_v = [&](uint16_t* buf, bool win) {
