@@ -138,6 +138,18 @@ VISIT_CASES = ["dense_g4", "dense_g2", "dense_g1", "window_sink4", "window_bigsi
 def test_visit_map_bit_exact(name):
     wl = _wl(name)
     _announce(f"visit map {name}")
+    _check_visit_map(wl)
+
+
+@pytest.mark.parametrize("window", [0, 150])
+def test_visit_map_messy_block_lists(window):
+    wl = _wl("blocks_g4", seed=9, window=window, n_sink=4 if window else 0)
+    wl.block_indices = _messy_block_lists(np.random.default_rng(21), wl.lengths, wl.hkv)
+    _announce(f"visit map messy block lists window={window}")
+    _check_visit_map(wl)
+
+
+def _check_visit_map(wl):
     q, k, v, cu, bi, sink = prefill_args(wl)
     got = sa.debug_visit_map(q, k, cu, wl.max_seqlen, wl.n_sink, wl.window, bi).cpu().numpy()
     qoff = np.concatenate([[0], np.cumsum(-(-wl.lengths // 64))])
@@ -222,6 +234,35 @@ def test_bwd_extreme_sinks(name, kind):
     wl = _wl(name, seed=11)
     wl.sink = _sink_values(kind, wl.hq)
     _announce(f"bwd extreme sink {name} a={kind}")
+    _check_bwd(wl)
+
+
+def _messy_block_lists(rng, lengths, hkv, width=6):
+    """Block lists the workload generator never draws but the mask accepts
+    ([Notes] s9-10: a query block attends to the key blocks its row lists):
+    entries in random order, one selected block listed twice, the block after
+    the query block (causally invisible), -1 between entries."""
+    rows = []
+    for L in lengths:
+        nqb = -(-int(L) // 64)
+        for qb in range(nqb):
+            for _g in range(hkv):
+                sel = [int(x) for x in rng.choice(qb + 1, size=min(qb + 1, 3), replace=False)]
+                sel.append(sel[0])
+                if qb + 1 < nqb:
+                    sel.append(qb + 1)
+                sel = (sel + [-1] * width)[:width]
+                rng.shuffle(sel)
+                rows.append(sel)
+    return np.asarray(rows, dtype=np.int32).reshape(-1, hkv, width)
+
+
+@pytest.mark.parametrize("window", [0, 150])
+def test_fwd_bwd_messy_block_lists(window):
+    wl = _wl("blocks_g4", seed=9, window=window, n_sink=4 if window else 0)
+    wl.block_indices = _messy_block_lists(np.random.default_rng(21), wl.lengths, wl.hkv)
+    _announce(f"fwd+bwd messy block lists window={window}")
+    check_fwd_full(wl, run_fwd(wl))
     _check_bwd(wl)
 
 
