@@ -78,6 +78,9 @@ FWD_CASES = {
     "dense_g8_long": dict(lengths=(1200, 70), hq=16, hkv=2),
     "window_split": dict(lengths=(2200,), hq=8, hkv=1, n_sink=4, window=256),
     "blocks_split": dict(lengths=(1500,), hq=16, hkv=2, block_lists=dict(n_random=4)),
+    # empty samples between and after others (cu_seqlens repeats a value)
+    "window_empty": dict(lengths=(130, 0, 70, 0), hq=4, hkv=2, n_sink=4, window=50),
+    "blocks_empty": dict(lengths=(0, 130, 0, 70), hq=4, hkv=2, block_lists=dict(n_random=2)),
 }
 
 
@@ -131,7 +134,8 @@ def test_fwd_dynamic_range_example():
 # ---------------------------------------------------------------------------
 
 VISIT_CASES = ["dense_g4", "dense_g2", "dense_g1", "window_sink4", "window_bigsink", "window_g2",
-               "window_one", "window_huge", "blocks_g4", "blocks_g1", "blocks_window", "blocks_nodiag"]
+               "window_one", "window_huge", "blocks_g4", "blocks_g1", "blocks_window", "blocks_nodiag",
+               "window_empty", "blocks_empty"]
 
 
 @pytest.mark.parametrize("name", VISIT_CASES)
@@ -187,7 +191,7 @@ BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "bl
              "d64_generic", "dense_g8_long", "window_split", "blocks_split", "dense_g1", "window_g2",
              "window_bigsink", "window_nosinktok", "window_wide", "window_one", "window_huge",
              "blocks_window", "dense_g3", "dense_g8", "stress_sink", "blocks_g1", "dense_g16", "dense_g5",
-             "window_g12"]
+             "window_g12", "window_empty", "blocks_empty"]
 
 
 def _check_bwd(wl):
