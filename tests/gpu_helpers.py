@@ -41,17 +41,19 @@ def prefill_args(wl: W.Prefill):
     return q, k, v, cu, bi, sink
 
 
-def run_fwd(wl: W.Prefill, args=None):
+def run_fwd(wl: W.Prefill, args=None, max_seqlen=None):
     q, k, v, cu, bi, sink = args if args is not None else prefill_args(wl)
-    o, lse, s = sa.fwd(q, k, v, cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+    ms = max_seqlen if max_seqlen is not None else wl.max_seqlen
+    o, lse, s = sa.fwd(q, k, v, cu, ms, wl.scale, wl.n_sink, wl.window, bi, sink)
     torch.cuda.synchronize()
     return o, lse, s
 
 
-def run_bwd(wl: W.Prefill, o, lse, args=None):
+def run_bwd(wl: W.Prefill, o, lse, args=None, max_seqlen=None):
     q, k, v, cu, bi, sink = args if args is not None else prefill_args(wl)
     do = dev(wl.do, wl.dtype)
-    g = sa.bwd(q, k, v, o, lse, do, cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+    ms = max_seqlen if max_seqlen is not None else wl.max_seqlen
+    g = sa.bwd(q, k, v, o, lse, do, cu, ms, wl.scale, wl.n_sink, wl.window, bi, sink)
     torch.cuda.synchronize()
     return g
 

@@ -194,10 +194,10 @@ BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "bl
              "window_g12", "window_empty", "blocks_empty"]
 
 
-def _check_bwd(wl):
+def _check_bwd(wl, max_seqlen=None):
     args = prefill_args(wl)
-    o, lse, s = run_fwd(wl, args)
-    dq, dk, dv, dsink = run_bwd(wl, o, lse, args)
+    o, lse, s = run_fwd(wl, args, max_seqlen)
+    dq, dk, dv, dsink = run_bwd(wl, o, lse, args, max_seqlen)
     kw = oracle_kwargs(wl)
     rdq, rdk, rdv, rds = oracle.bwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale,
                                     wl.do.f32, **kw)
@@ -268,6 +268,18 @@ def test_fwd_bwd_messy_block_lists(window):
     _announce(f"fwd+bwd messy block lists window={window}")
     check_fwd_full(wl, run_fwd(wl))
     _check_bwd(wl)
+
+
+@pytest.mark.parametrize("name", ["window_sink4", "dense_g8_long", "blocks_g4", "d64_generic"])
+def test_fwd_bwd_max_seqlen_above_every_sample(name):
+    """max_seqlen is an upper bound on the lengths: with four times the
+    longest sample, the workgroups and key tiles past every sample do no work
+    and the results match the oracle as before."""
+    wl = _wl(name, seed=4)
+    ms = 4 * wl.max_seqlen
+    _announce(f"fwd+bwd max_seqlen x4 {name}")
+    check_fwd_full(wl, run_fwd(wl, max_seqlen=ms))
+    _check_bwd(wl, max_seqlen=ms)
 
 
 def test_bwd_is_repeatable():
