@@ -146,3 +146,26 @@ def check_fwd_full(wl: W.Prefill, out):
         assert err <= tol["s"], f"s: max abs err {err:.3e}"
     return ro, rl, rs
 
+
+
+def check_bwd_full(wl: W.Prefill, max_seqlen=None):
+    """Forward, then backward, against the oracle: dQ, dK, dV to the gradient
+    bound, dsink max-normalised and head by head (with the floor that the
+    output type's rounding of O allows)."""
+    args = prefill_args(wl)
+    o, lse, s = run_fwd(wl, args, max_seqlen)
+    dq, dk, dv, dsink = run_bwd(wl, o, lse, args, max_seqlen)
+    kw = oracle_kwargs(wl)
+    rdq, rdk, rdv, rds = oracle.bwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale,
+                                    wl.do.f32, **kw)
+    tol = tol_for(wl.dtype)
+    assert_grad(host(dq), rdq, tol, "dQ")
+    assert_grad(host(dk), rdk, tol, "dK")
+    assert_grad(host(dv), rdv, tol, "dV")
+    if wl.sink is not None:
+        ro, rl, _ = oracle.fwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, **kw)
+        assert_dsink(host(dsink), rds, tol)
+        floor = dsink_storage_floor(ro, wl.do.f32, rl, wl.sink, wl.dtype)
+        assert_dsink_per_head(host(dsink), rds, tol, floor)
+    else:
+        assert dsink is None

@@ -9,9 +9,9 @@ import oracle
 import streamingllm_sink_attn_amd as sa
 from streamingllm_sink_attn_amd import workloads as W
 
-from gpu_helpers import (DEV, assert_dsink, assert_dsink_per_head, assert_grad, assert_lse, assert_out,
-                         check_fwd_full, dev, dsink_storage_floor, host, oracle_kwargs, prefill_args,
-                         run_bwd, run_fwd, tol_for)
+from gpu_helpers import (DEV, assert_dsink, assert_grad, assert_lse, assert_out, check_bwd_full,
+                         check_fwd_full, dev, host, oracle_kwargs, prefill_args, run_bwd, run_fwd,
+                         tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -195,23 +195,7 @@ BWD_CASES = ["dense_g4", "window_sink4", "blocks_g4", "no_sink", "dense_g2", "bl
 
 
 def _check_bwd(wl, max_seqlen=None):
-    args = prefill_args(wl)
-    o, lse, s = run_fwd(wl, args, max_seqlen)
-    dq, dk, dv, dsink = run_bwd(wl, o, lse, args, max_seqlen)
-    kw = oracle_kwargs(wl)
-    rdq, rdk, rdv, rds = oracle.bwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale,
-                                    wl.do.f32, **kw)
-    tol = tol_for(wl.dtype)
-    assert_grad(host(dq), rdq, tol, "dQ")
-    assert_grad(host(dk), rdk, tol, "dK")
-    assert_grad(host(dv), rdv, tol, "dV")
-    if wl.sink is not None:
-        ro, rl, _ = oracle.fwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, **kw)
-        assert_dsink(host(dsink), rds, tol)
-        floor = dsink_storage_floor(ro, wl.do.f32, rl, wl.sink, wl.dtype)
-        assert_dsink_per_head(host(dsink), rds, tol, floor)
-    else:
-        assert dsink is None
+    check_bwd_full(wl, max_seqlen)
 
 
 @pytest.mark.parametrize("name", BWD_CASES)
