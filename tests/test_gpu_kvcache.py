@@ -219,6 +219,7 @@ def _prefill_stream(rng, B, hq, hkv, d, n_sink, window, quantized, chunks, start
         sa.kvcache_append(cache, kt, vt, st)
         KO.append(ref, k, v, seen, n_sink, window)
         seen = seen + c
+    return cache, ref, seen
 
 
 @pytest.mark.parametrize("quantized", [False, True])
@@ -340,3 +341,33 @@ def test_cache_calls_without_s(d):
         a = sa.kvcache_decode(cache, q1, seen, 0.1, sink)
         b = sa.kvcache_decode(cache, q1, seen, 0.1, sink, return_s=False)
         assert b[2] is None and torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Seeded random streams: every call of the cache API on one stream
+# ---------------------------------------------------------------------------
+
+def _random_stream_case(i):
+    rng = np.random.default_rng(9100 + i)
+    quantized = bool(i % 2)
+    B = int(rng.integers(1, 4))
+    hkv = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    d = 128 if quantized else int(rng.choice([128, 128, 64]))
+    n_sink = int(rng.choice([0, 1, 3, 4, 6, 64]))
+    window = int(rng.integers(1, 301))
+    chunks = [int(x) for x in rng.integers(1, 201, size=int(rng.integers(1, 5)))]
+    start = [int(x) for x in rng.integers(0, 501, size=B)] if rng.random() < 0.5 else None
+    return rng, quantized, B, hkv * G, hkv, d, n_sink, window, chunks, start
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_streams(i):
+    """Random cache shapes and chunk sequences: each chunk's prefill against
+    the cache and its append compared with the oracle, then a decode over
+    the final cache with a random split count."""
+    rng, quantized, B, hq, hkv, d, n_sink, window, chunks, start = _random_stream_case(i)
+    print(f"[case] kvcache random stream {i}: q={quantized} B={B} hq={hq} hkv={hkv} d={d} "
+          f"n_sink={n_sink} window={window} chunks={chunks} start={start}", flush=True)
+    cache, ref, seen = _prefill_stream(rng, B, hq, hkv, d, n_sink, window, quantized, chunks, start)
+    _check_decode(cache, ref, seen, n_sink, window, hq, int(rng.choice([0, 1, 3])), rng)
