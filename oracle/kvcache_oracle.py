@@ -17,7 +17,7 @@ Sources (cited by title and section):
   [Blog] "Attention Sink" (lijianxiong.space), H2O section: the recent part is
          a circular queue whose oldest entry the new token replaces.
 
-Readings (each is listed in DESIGN.md):
+Readings where the pages leave a step open:
   * Placement: the token at stream position p lives in sink slot p when
     p < n_sink, else in ring slot (p - n_sink) mod W of the window segment.
     After T tokens the cache holds positions [0, min(T, n_sink)) and

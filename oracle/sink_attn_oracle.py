@@ -31,7 +31,7 @@ Gate statistics:
              (the first token of the sample plays the sink: G = 1 - A_0, s2)
   Imp_h    = (1/|T|) sum_i G_ih                    [MoE] s4, head importance
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * g(h) = h // (Hq / Hkv): contiguous groups of query heads share a KV head.
   * window W > 0: key j is in the window of query i iff i - j < W (the query
     itself counts); the first n_sink tokens of each sample stay visible.
