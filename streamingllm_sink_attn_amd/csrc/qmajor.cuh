@@ -47,10 +47,11 @@ inline Geo make_geo(const Prefill& p, int nw, int qw) {
 }
 
 // Flat block id -> coordinates: sample slowest, then position tiles heaviest
-// (latest) first, then (KV head, head group) fastest.  Consecutive ids go to
-// the XCDs round-robin, so with Z a multiple of 8 every XCD serves fixed KV
-// heads, and working one sample at a time keeps that sample's K/V slice of
-// each KV head resident in the XCD's L2.
+// (latest) first, then (head group, KV head) fastest, KV head fastest of all.
+// Consecutive ids go to the XCDs round-robin, so with Hkv a multiple of 8
+// every XCD serves fixed KV heads, all head groups of a KV head on the same
+// XCD, and working one sample at a time keeps that sample's K/V slice of each
+// KV head resident in the XCD's L2.
 struct WgCoord {
   int pt, b, g, hg;
 };
@@ -61,8 +62,9 @@ __device__ __forceinline__ WgCoord wg_coord(const Geo& geo, int batch, int bid) 
   const int rem = bid % per_b;
   c.pt = geo.nptiles - 1 - rem / geo.Z;
   const int z = rem % geo.Z;
-  c.g = z / geo.nhg;
-  c.hg = z % geo.nhg;
+  const int hkv = geo.Z / geo.nhg;
+  c.g = z % hkv;
+  c.hg = z / hkv;
   (void)batch;
   return c;
 }
