@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ('fwd_mfma.hip', 'qmajor.cuh', 'common.cuh', 'internal.h', 'stream_rows.cuh'),
-    "sha256": "e4ef8bd8c7e6e30bd925bd3ba42f55d3bcbd5276c81d15f9bcce3204204ba274",
-    "read_bytes": 231041760,
-    "write_bytes": 142688087,
+    "sha256": "028ac344b7ddeb8903a0d255c42509061a79326bef57d25e74232fc8b41ac2b2",
+    "read_bytes": 231095782,
+    "write_bytes": 142681718,
 }
 
 
