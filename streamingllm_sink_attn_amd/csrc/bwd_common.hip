@@ -18,7 +18,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(Prefill p, const void* __restrict__ o,
                                                              const float* __restrict__ lse,
                                                              const void* __restrict__ dout,
-                                                             BwdWork w, int zero_dq) {
+                                                             BwdWork w) {
   constexpr int kPerChunk = 16 / sizeof(T);
   const int D = p.d;
   const int nchunks = D / kPerChunk;
@@ -47,10 +47,6 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(Prefill p, const vo
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (zero_dq) {
-      for (int e = sub * 4; e < D; e += 64)
-        *reinterpret_cast<f32x4*>(w.dq_acc + row * D + e) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     if (sub == 0) {
       const int h = static_cast<int>(row % p.hq);
       const float L = lse[row];
@@ -112,17 +108,15 @@ hipError_t launch_fill_zero_bytes(uint8_t* ptr, size_t n, hipStream_t st) {
 }
 
 hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* lse,
-                                 const void* dout, const BwdWork& w, bool zero_dq,
-                                 bool zero_dkv, hipStream_t st) {
+                                 const void* dout, const BwdWork& w, bool zero_dkv, hipStream_t st) {
   if (p.total == 0) return hipSuccess;
   const size_t R = static_cast<size_t>(p.total) * p.hq;
   const int grid = grid_for(R, 16);
   if (p.dtype == SINK_ATTN_F32)
-    hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(256), 0, st, p, o, lse, dout,
-                       w, zero_dq ? 1 : 0);
+    hipLaunchKernelGGL(bwd_preprocess_kernel<float>, dim3(grid), dim3(256), 0, st, p, o, lse, dout, w);
   else
     hipLaunchKernelGGL(bwd_preprocess_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, p, o, lse,
-                       dout, w, zero_dq ? 1 : 0);
+                       dout, w);
   if (zero_dkv) {
     const size_t n = static_cast<size_t>(p.total) * p.hkv * p.d;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 1024)), dim3(256), 0, st, w.dk_acc, n);
@@ -335,15 +329,11 @@ static void convert(const float* src, void* dst, size_t n, hipStream_t st) {
   hipLaunchKernelGGL(convert_kernel<T>, dim3(grid_for(n, 1024)), dim3(256), 0, st, src, dst, n);
 }
 
-hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq, void* dk,
-                             void* dv, bool dq_from_acc, bool dkv_from_acc, hipStream_t st) {
+hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dk, void* dv,
+                             bool dkv_from_acc, hipStream_t st) {
   if (dsink != nullptr) launch_column_sum(w.dsink_terms, p.total, p.hq, 1.f, w.dsink_part, dsink, st);
-  const size_t nq = static_cast<size_t>(p.total) * p.hq * p.d;
   const size_t nkv = static_cast<size_t>(p.total) * p.hkv * p.d;
   const bool f32 = p.dtype == SINK_ATTN_F32;
-  if (dq_from_acc) {
-    if (f32) convert<float>(w.dq_acc, dq, nq, st); else convert<uint16_t>(w.dq_acc, dq, nq, st);
-  }
   if (dkv_from_acc) {
     if (f32) {
       convert<float>(w.dk_acc, dk, nkv, st);

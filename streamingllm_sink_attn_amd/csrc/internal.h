@@ -35,7 +35,6 @@ struct BwdWork {
   float* lnew;       // [T, Hq]  log2(e) * log(Z + e^a) (or of L_orig; +inf for empty rows without a sink)
   float* dsink_terms;// [T, Hq]  -Delta * p_sink per row
   float* dsink_part; // [ceil(T/64), Hq] per-slab partial sums of the terms
-  float* dq_acc;     // [T, Hq, D]  (MFMA path) accumulated dQ
   float* dk_acc;     // generic path: [T, Hkv, D]; MFMA path: [max split tiles, 64, D] (split key tiles)
   float* dv_acc;     // as dk_acc
   int32_t* csr_off;  // [nqb*Hkv + 1]  (block mode) per (KV block, KV head) list offsets
@@ -101,9 +100,9 @@ bool fwd_mfma_supported(const Prefill& p);
 hipError_t launch_fwd_mfma_cache(const Prefill& p, const CacheKv& ckv, const void* q, void* o, float* lse,
                                  float* s, hipStream_t st);
 
+// zero_dkv: also zero the float32 dK/dV accumulators of every row (generic path).
 hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* lse,
-                                 const void* dout, const BwdWork& w, bool zero_dq,
-                                 bool zero_dkv, hipStream_t st);
+                                 const void* dout, const BwdWork& w, bool zero_dkv, hipStream_t st);
 hipError_t launch_bwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
                               const void* dout, const BwdWork& w, void* dq, hipStream_t st);
 // Key-major dK/dV kernel followed by the query-major dQ kernel.
@@ -124,9 +123,8 @@ int dsink_slabs(int total);                 // row slabs of the dsink reduction
 // order): deterministic.
 hipError_t launch_column_sum(const float* x, int rows, int cols, float scale, float* part,
                              float* out, hipStream_t st);
-hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dq,
-                             void* dk, void* dv, bool dq_from_acc, bool dkv_from_acc,
-                             hipStream_t st);
+hipError_t launch_bwd_finish(const Prefill& p, const BwdWork& w, float* dsink, void* dk, void* dv,
+                             bool dkv_from_acc, hipStream_t st);
 
 hipError_t launch_decode(const Decode& p, const void* q, const void* kc, const void* vc,
                          void* o, float* lse, float* s, float* ws, hipStream_t st);

@@ -95,7 +95,7 @@ size_t elem_size(int dtype) { return dtype == SINK_ATTN_F32 ? 4 : 2; }
 
 // Backward workspace layout (each section 256-byte aligned).
 struct BwdLayout {
-  size_t delta, lnew, terms, dsink_part, dq_acc, dk_acc, dv_acc, csr_off, csr_idx, csr_bits, plan, split_slot,
+  size_t delta, lnew, terms, dsink_part, dk_acc, dv_acc, csr_off, csr_idx, csr_bits, plan, split_slot,
       queues, total;
   int max_split;
 };
@@ -110,7 +110,6 @@ BwdLayout bwd_layout(const sa::Prefill& p) {
   l.lnew = off; off += round_up(rows * 4);
   l.terms = off; off += round_up(rows * 4);
   l.dsink_part = off; off += round_up(static_cast<size_t>(sa::dsink_slabs(p.total)) * p.hq * 4);
-  l.dq_acc = off;                                   // unused: dQ is stored directly
   // float32 dK/dV: every row on the generic path, split key tiles only on the
   // matrix-core path (64 rows of D per tile)
   l.max_split = mfma ? sa::bwd_max_split_tiles(p) : 0;
@@ -466,7 +465,6 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     w.lnew = reinterpret_cast<float*>(base + lay.lnew);
     w.dsink_terms = reinterpret_cast<float*>(base + lay.terms);
     w.dsink_part = reinterpret_cast<float*>(base + lay.dsink_part);
-    w.dq_acc = reinterpret_cast<float*>(base + lay.dq_acc);
     w.dk_acc = reinterpret_cast<float*>(base + lay.dk_acc);
     w.dv_acc = reinterpret_cast<float*>(base + lay.dv_acc);
     w.csr_off = reinterpret_cast<int32_t*>(base + lay.csr_off);
@@ -479,14 +477,14 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     const bool mfma = sa::bwd_mfma_supported(p);
     hipError_t e;
     if (mfma) {
-      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dq=*/false, /*zero_dkv=*/false, st);
+      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dkv=*/false, st);
       if (e == hipSuccess && p.blocks != nullptr) e = sa::launch_block_csr(p, w, st);
       if (e == hipSuccess) e = sa::launch_bwd_mfma(p, q, k, v, dout, w, dq, dk, dv, st);
-      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dq, dk, dv, false, false, st);
+      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dk, dv, /*dkv_from_acc=*/false, st);
     } else {
-      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, false, true, st);
+      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dkv=*/true, st);
       if (e == hipSuccess) e = sa::launch_bwd_generic(p, q, k, v, dout, w, dq, st);
-      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dq, dk, dv, false, true, st);
+      if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dk, dv, /*dkv_from_acc=*/true, st);
     }
     return hip_status(e, "sink_attn_bwd launch");
   } catch (...) {
