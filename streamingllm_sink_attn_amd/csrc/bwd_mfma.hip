@@ -17,7 +17,7 @@
 //     reverse lists).
 //   * Tiles differ a lot in work (a first-token tile, or block 0 that every
 //     block list selects, is seen by every query tile), so a planning kernel
-//     cuts every tile's iterations into chunks of at most kChunk and a
+//     cuts every tile's iterations into chunks of at most item_iters(p) and a
 //     persistent kernel pulls chunks from work queues (one per XCD, keyed by
 //     KV head, so one XCD's L2 streams one head group's Q/dO).  A tile done in
 //     one chunk writes bf16 dK/dV directly; a split tile adds its chunks'
@@ -46,7 +46,20 @@ using namespace qm;
 
 constexpr int BM = 64;            // query rows per iteration
 constexpr int NWK = 2;            // wavefronts per workgroup
-constexpr int kChunk = 128;       // iterations per work item
+constexpr int kChunkMax = 256;    // most iterations per work item
+
+// Iterations per work item.  Window and causal key tiles have few iterations
+// each (at most (W + 62) / 64 + 1 query tiles times G), and finer items
+// balance the queues' tails better; a key tile of the block lists is seen by
+// G x (about 17 on average) iterations, so the longer item keeps most tiles
+// whole instead of splitting them into float32 partials.  (Measured: window
+// 1024, G = 4: dK/dV 1,255 us at 128, 1,369 us at 192; 17 blocks, G = 8:
+// 6,174 us at 128, 6,072 us at 256, and half the split-tile passes.)
+constexpr int kItemDense = 128, kItemBlocks = 256;
+static_assert(kItemDense <= kChunkMax && kItemBlocks <= kChunkMax, "item fits the LDS iteration table");
+__host__ __device__ inline int item_iters(const Prefill& p) {
+  return p.blocks != nullptr ? kItemBlocks : kItemDense;
+}
 constexpr int kMaxQueues = 8;
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -118,7 +131,8 @@ __global__ __launch_bounds__(256) void plan_kernel(Prefill p, BwdWork w, int nkt
   if (t.kt * BN < L) {
     const TileWork tw = tile_work(p, w, t.b, t.kt, t.g, L);
     const int n = tw.per_head * (p.hq / p.hkv);
-    chunks = max(1, (n + kChunk - 1) / kChunk);
+    const int per_item = item_iters(p);
+    chunks = max(1, (n + per_item - 1) / per_item);
   }
   w.plan[ti + 1] = chunks;
   w.split_slot[ti + 1] = chunks > 1 ? 1 : 0;
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
   __shared__ __attribute__((aligned(16))) uint16_t dobuf[2][TILE];
   __shared__ __attribute__((aligned(16))) float lbuf[2][BM];
   __shared__ __attribute__((aligned(16))) float dbuf[2][BM];
-  __shared__ int qt_tab[kChunk];     // query head and tile of each iteration of the item
+  __shared__ int qt_tab[kChunkMax];  // query head and tile of each iteration of the item
   __shared__ int item_sh;
 
   const int tid = threadIdx.x;
@@ -273,8 +287,8 @@ __global__ __launch_bounds__(128, 2) void dkdv_kernel(Prefill p, int nkt, int nq
     const int kw0 = k0 + 32 * wv;                 // this wavefront's first key
     const TileWork tw = tile_work(p, w, b, kt, g, L);
     const int n_all = G * tw.per_head;
-    const int it_begin = chunk * kChunk;
-    const int it_end = min(n_all, it_begin + kChunk);
+    const int it_begin = chunk * item_iters(p);
+    const int it_end = min(n_all, it_begin + item_iters(p));
 
     // K, V as B operands (lane: key kw0 + l32, dims gq*64 + ks*8)
     bf16x8 kB[8], vB[8];
@@ -512,13 +526,13 @@ int bwd_num_tiles(const Prefill& p) {
 }
 
 // A key tile splits when its iterations (query tiles or reverse-list entries
-// seeing it, times the G query heads of its group) exceed kChunk, i.e. when
-// more than cap = kChunk / G query tiles see it.
+// seeing it, times the G query heads of its group) exceed item_iters(p), i.e.
+// when more than cap = item_iters(p) / G query tiles see it.
 int bwd_max_split_tiles(const Prefill& p) {
   const long long ntiles = bwd_num_tiles(p);
   const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
   const int G = p.hq / p.hkv;
-  const long long cap = bwd128::kChunk / G;
+  const long long cap = bwd128::item_iters(p) / G;
   long long bound = ntiles;
   if (p.blocks != nullptr) {
     // every reverse-list entry comes from one block_indices entry
