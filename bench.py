@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ('fwd_mfma.hip', 'qmajor.cuh', 'common.cuh', 'internal.h', 'stream_rows.cuh'),
-    "sha256": "028ac344b7ddeb8903a0d255c42509061a79326bef57d25e74232fc8b41ac2b2",
-    "read_bytes": 231095782,
-    "write_bytes": 142681718,
+    "sha256": "fa71a6a0686d95338b090d7811f7a90a4aca73faf57284186dad6f39b2d478ba",
+    "read_bytes": 231316048,
+    "write_bytes": 142686052,
 }
 
 
