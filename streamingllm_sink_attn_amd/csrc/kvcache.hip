@@ -20,16 +20,18 @@ namespace kvc {
 
 constexpr float kE4m3Max = 448.f;
 
-// 16 lanes per (sequence b, chunk token c, KV head g), 16-byte pieces: writes
-// the K and V rows of the token to its slot, or nothing when a later token of
-// the same chunk takes that slot (only the last `window` non-first tokens
-// survive, so no slot gets two writers).
+// 8 lanes per (sequence b, chunk token c, KV head g), every load of a lane
+// issued before its first store: writes the K and V rows of the token to its
+// slot, or nothing when a later token of the same chunk takes that slot (only
+// the last `window` non-first tokens survive, so no slot gets two writers).
+constexpr int kAppendLanes = 8;      // lanes per row
+constexpr int kAppendPieces = 2;     // 16-byte pieces of K and of V per lane and pass
 template <bool QUANT>
 __global__ __launch_bounds__(256) void append_kernel(KvCache c, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, int chunk,
                                                      const int32_t* __restrict__ n_seen) {
-  const size_t unit = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+  const size_t unit = static_cast<size_t>(blockIdx.x) * (256 / kAppendLanes) + threadIdx.x / kAppendLanes;
+  const int sub = threadIdx.x % kAppendLanes;
   if (unit >= static_cast<size_t>(c.batch) * chunk * c.hkv) return;
   const int g = static_cast<int>(unit % c.hkv);
   const int cc = static_cast<int>((unit / c.hkv) % chunk);
@@ -56,43 +58,69 @@ __global__ __launch_bounds__(256) void append_kernel(KvCache c, const uint16_t* 
       dk = static_cast<uint16_t*>(c.sink_k) + dst;
       dv = static_cast<uint16_t*>(c.sink_v) + dst;
     }
-    for (int e = sub; e < D / 8; e += 16) {
-      *reinterpret_cast<u32x4*>(dk + 8 * e) = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
-      *reinterpret_cast<u32x4*>(dv + 8 * e) = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
+    // pieces sub, sub + 8, ...: each load instruction reads 128 contiguous
+    // bytes; one pass covers a row of head_dim 128
+    const int np = D / 8;
+    for (int e0 = 0; e0 < np; e0 += kAppendLanes * kAppendPieces) {
+      u32x4 kp[kAppendPieces], vp[kAppendPieces];
+#pragma unroll
+      for (int j = 0; j < kAppendPieces; ++j) {
+        const int e = e0 + sub + kAppendLanes * j;
+        if (e < np) {
+          kp[j] = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
+          vp[j] = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kAppendPieces; ++j) {
+        const int e = e0 + sub + kAppendLanes * j;
+        if (e < np) {
+          *reinterpret_cast<u32x4*>(dk + 8 * e) = kp[j];
+          *reinterpret_cast<u32x4*>(dv + 8 * e) = vp[j];
+        }
+      }
     }
     return;
   }
 
-  // 8-bit ring row (head_dim 128: 8 values per lane): amax over the row, then
-  // the codes, two per conversion.
+  // 8-bit ring row (head_dim 128): lane sub holds values 16 sub .. 16 sub + 15
+  // of the K row and of the V row; amax over the row, then the codes, two per
+  // conversion, 16 contiguous bytes per lane.
   const size_t dst = ((static_cast<size_t>(b) * c.window + ring) * c.hkv + g) * D;
   const size_t sidx = (static_cast<size_t>(b) * c.hkv + g) * c.window + ring;
+  u32x4 raw[2][2];                                       // [K, V][piece]
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      raw[which][j] = *reinterpret_cast<const u32x4*>((which == 0 ? k_new : v_new) + src + 16 * sub + 8 * j);
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>((which == 0 ? k_new : v_new) + src + 8 * sub);
-    float xv[8];
+    float xv[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xv[2 * j] = __uint_as_float(raw[j] << 16);
-      xv[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[8 * j + 2 * q] = __uint_as_float(raw[which][j][q] << 16);
+        xv[8 * j + 2 * q + 1] = __uint_as_float(raw[which][j][q] & 0xffff0000u);
+      }
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(xv[j]));
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(xv[j]));
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    for (int off = kAppendLanes / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kAppendLanes));
     const float scale = amax > 0.f ? amax / kE4m3Max : 0.f;
     const float inv = amax > 0.f ? kE4m3Max / amax : 0.f;
-    u32x2 codes = {0u, 0u};
+    u32x4 codes = {0u, 0u, 0u, 0u};
     if (amax > 0.f) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 4; ++j) {
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(xv[4 * j] * inv, xv[4 * j + 1] * inv, 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(xv[4 * j + 2] * inv, xv[4 * j + 3] * inv, w, true);
         codes[j] = static_cast<uint32_t>(w);
       }
     }
-    *reinterpret_cast<u32x2*>((which == 0 ? c.win_k : c.win_v) + dst + 8 * sub) = codes;
+    *reinterpret_cast<u32x4*>((which == 0 ? c.win_k : c.win_v) + dst + 16 * sub) = codes;
     if (sub == 0) (which == 0 ? c.win_k_scale : c.win_v_scale)[sidx] = scale;
   }
 }
@@ -304,8 +332,9 @@ hipError_t launch_kvcache_append(const KvCache& c, const void* k_new, const void
   const long long rows = static_cast<long long>(c.batch) * chunk * c.hkv;
   if (rows <= 0) return hipSuccess;
   auto kern = c.quantized ? kvc::append_kernel<true> : kvc::append_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st, c,
-                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), chunk,
+  constexpr int per_block = 256 / kvc::kAppendLanes;        // rows per workgroup
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((rows + per_block - 1) / per_block)), dim3(256), 0, st,
+                     c, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), chunk,
                      n_seen);
   return hipGetLastError();
 }
