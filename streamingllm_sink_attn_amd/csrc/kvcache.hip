@@ -26,6 +26,32 @@ constexpr float kE4m3Max = 448.f;
 // the last `window` non-first tokens survive, so no slot gets two writers).
 constexpr int kAppendLanes = 8;      // lanes per row
 constexpr int kAppendPieces = 2;     // 16-byte pieces of K and of V per lane and pass
+
+// Copies a K row and a V row of n 16-byte pieces with kAppendLanes lanes:
+// pieces sub, sub + 8, ... (each load instruction reads 128 contiguous bytes),
+// every load of a pass issued before its stores.
+__device__ __forceinline__ void copy_rows(const uint16_t* ks, const uint16_t* vs, uint16_t* kd, uint16_t* vd,
+                                          int n, int sub) {
+  for (int e0 = 0; e0 < n; e0 += kAppendLanes * kAppendPieces) {
+    u32x4 kr[kAppendPieces], vr[kAppendPieces];
+#pragma unroll
+    for (int j = 0; j < kAppendPieces; ++j) {
+      const int e = e0 + sub + kAppendLanes * j;
+      if (e < n) {
+        kr[j] = *reinterpret_cast<const u32x4*>(ks + 8 * e);
+        vr[j] = *reinterpret_cast<const u32x4*>(vs + 8 * e);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kAppendPieces; ++j) {
+      const int e = e0 + sub + kAppendLanes * j;
+      if (e < n) {
+        *reinterpret_cast<u32x4*>(kd + 8 * e) = kr[j];
+        *reinterpret_cast<u32x4*>(vd + 8 * e) = vr[j];
+      }
+    }
+  }
+}
 template <bool QUANT>
 __global__ __launch_bounds__(256) void append_kernel(KvCache c, const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new, int chunk,
@@ -58,28 +84,7 @@ __global__ __launch_bounds__(256) void append_kernel(KvCache c, const uint16_t* 
       dk = static_cast<uint16_t*>(c.sink_k) + dst;
       dv = static_cast<uint16_t*>(c.sink_v) + dst;
     }
-    // pieces sub, sub + 8, ...: each load instruction reads 128 contiguous
-    // bytes; one pass covers a row of head_dim 128
-    const int np = D / 8;
-    for (int e0 = 0; e0 < np; e0 += kAppendLanes * kAppendPieces) {
-      u32x4 kp[kAppendPieces], vp[kAppendPieces];
-#pragma unroll
-      for (int j = 0; j < kAppendPieces; ++j) {
-        const int e = e0 + sub + kAppendLanes * j;
-        if (e < np) {
-          kp[j] = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
-          vp[j] = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kAppendPieces; ++j) {
-        const int e = e0 + sub + kAppendLanes * j;
-        if (e < np) {
-          *reinterpret_cast<u32x4*>(dk + 8 * e) = kp[j];
-          *reinterpret_cast<u32x4*>(dv + 8 * e) = vp[j];
-        }
-      }
-    }
+    copy_rows(k_new + src, v_new + src, dk, dv, D / 8, sub);
     return;
   }
 
@@ -212,8 +217,8 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const ui
                                                              uint16_t* __restrict__ qp, int32_t* __restrict__ cu,
                                                              int32_t* __restrict__ qstart,
                                                              int32_t* __restrict__ qo_base) {
-  const size_t unit = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+  const size_t unit = static_cast<size_t>(blockIdx.x) * (256 / kAppendLanes) + threadIdx.x / kAppendLanes;
+  const int sub = threadIdx.x % kAppendLanes;
   const size_t units = static_cast<size_t>(c.batch) * lmax * c.hkv;
   if (unit >= units) return;
   const int g = static_cast<int>(unit % c.hkv);
@@ -239,16 +244,13 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const ui
   if (i >= sg.ns + sg.nw) {                           // a chunk token
     const int cc = i - sg.ns - sg.nw;
     const size_t src = ((static_cast<size_t>(b) * chunk + cc) * c.hkv + g) * D;
-    for (int e = sub; e < nchunk8; e += 16) {
-      *reinterpret_cast<u32x4*>(kp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(k_new + src + 8 * e);
-      *reinterpret_cast<u32x4*>(vp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(v_new + src + 8 * e);
-    }
+    copy_rows(k_new + src, v_new + src, kp + dst, vp + dst, nchunk8, sub);
     const int G = qp != nullptr ? hq / c.hkv : 0;    // Q rows only for a packed copy
     for (int hh = 0; hh < G; ++hh) {
       const int h = g * G + hh;
       const size_t qs = ((static_cast<size_t>(b) * chunk + cc) * hq + h) * D;
       const size_t qd = ((static_cast<size_t>(b) * lmax + i) * hq + h) * D;
-      for (int e = sub; e < nchunk8; e += 16)
+      for (int e = sub; e < nchunk8; e += kAppendLanes)
         *reinterpret_cast<u32x4*>(qp + qd + 8 * e) = *reinterpret_cast<const u32x4*>(q + qs + 8 * e);
     }
     return;
@@ -269,32 +271,37 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(KvCache c, const ui
       sk = static_cast<const uint16_t*>(c.sink_k) + o;
       sv = static_cast<const uint16_t*>(c.sink_v) + o;
     }
-    for (int e = sub; e < nchunk8; e += 16) {
-      *reinterpret_cast<u32x4*>(kp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(sk + 8 * e);
-      *reinterpret_cast<u32x4*>(vp + dst + 8 * e) = *reinterpret_cast<const u32x4*>(sv + 8 * e);
-    }
+    copy_rows(sk, sv, kp + dst, vp + dst, nchunk8, sub);
     return;
   }
-  // 8-bit ring row: code * scale in float32, rounded to bfloat16.
+  // 8-bit ring row (head_dim 128): code * scale in float32, rounded to
+  // bfloat16; lane sub converts pieces sub and sub + 8 of K and of V, its
+  // loads issued before its stores.
   const size_t o = ((static_cast<size_t>(b) * c.window + ring) * c.hkv + g) * D;
   const size_t si = (static_cast<size_t>(b) * c.hkv + g) * c.window + ring;
+  u32x2 w[2][2];                                      // [K, V][piece]
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      w[which][j] = *reinterpret_cast<const u32x2*>((which == 0 ? c.win_k : c.win_v) + o +
+                                                    8 * (sub + kAppendLanes * j));
+  const float scs[2] = {c.win_k_scale[si], c.win_v_scale[si]};
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const uint8_t* codes = (which == 0 ? c.win_k : c.win_v) + o;
-    const float sc = (which == 0 ? c.win_k_scale : c.win_v_scale)[si];
     uint16_t* out = (which == 0 ? kp : vp) + dst;
-    for (int e = sub; e < nchunk8; e += 16) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(codes + 8 * e);
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
       u32x4 r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t word = w[j >> 1];
+        const uint32_t word = w[which][jp][j >> 1];
         const auto f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true)
                                : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        bf16x2 v2 = {static_cast<__bf16>(f[0] * sc), static_cast<__bf16>(f[1] * sc)};
+        bf16x2 v2 = {static_cast<__bf16>(f[0] * scs[which]), static_cast<__bf16>(f[1] * scs[which])};
         r[j] = __builtin_bit_cast(uint32_t, v2);
       }
-      *reinterpret_cast<u32x4*>(out + 8 * e) = r;
+      *reinterpret_cast<u32x4*>(out + 8 * (sub + kAppendLanes * jp)) = r;
     }
   }
 }
@@ -346,7 +353,8 @@ hipError_t launch_kvcache_prefill_gather(const KvCache& c, const void* q, const 
   const size_t units = static_cast<size_t>(c.batch) * lmax * c.hkv;
   if (units == 0) return hipSuccess;
   auto kern = c.quantized ? kvc::prefill_gather_kernel<true> : kvc::prefill_gather_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((units + 15) / 16)), dim3(256), 0, st, c,
+  constexpr int per_block = 256 / kvc::kAppendLanes;        // rows per workgroup
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((units + per_block - 1) / per_block)), dim3(256), 0, st, c,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), chunk, hq, n_seen, lmax, static_cast<uint16_t*>(kp),
                      static_cast<uint16_t*>(vp), static_cast<uint16_t*>(qp), cu, qstart, qo_base);
