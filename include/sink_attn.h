@@ -337,6 +337,15 @@ int sink_attn_head_importance(const float* gate, int32_t rows, int32_t num_heads
  *   dsink     output float32 [Hq]; required when desc->learnable_sink is
  *             non-NULL and must be NULL otherwise.  Reduced in a fixed order
  *             (deterministic).  The caller casts it to the parameter dtype.
+ * Streams: on the matrix-core path the dQ pass runs on a second stream the
+ * library owns (one per device, default priority, created by the first call
+ * on that device made outside graph capture) beside the dK/dV pass on
+ * `stream`; it is forked from `stream` after the preprocess and joined back
+ * before the call returns, so all work of the call is ordered before later
+ * work on `stream` (under capture: graph edges).  Concurrent calls on one
+ * device take turns through the fork and join.  SINK_ATTN_SERIAL_BWD=1 in
+ * the environment (read on every call) keeps everything on `stream`; the
+ * results are the same either way.
  */
 int sink_attn_bwd(const sink_attn_prefill_desc* desc,
                   const void* q, const void* k, const void* v,

@@ -552,13 +552,10 @@ int bwd_max_split_tiles(const Prefill& p) {
   return static_cast<int>(std::min(ntiles, std::max(0LL, bound)));
 }
 
-hipError_t launch_bwd_dq(const Prefill& p, const void* q, const void* k, const void* v,
-                         const void* dout, const BwdWork& w, void* dq, hipStream_t st);
 hipError_t launch_scan(int32_t* off, int n, hipStream_t st);
 
-hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
-                           const void* dout, const BwdWork& w, void* dq, void* dk, void* dv,
-                           hipStream_t st) {
+hipError_t launch_bwd_dkdv(const Prefill& p, const void* q, const void* k, const void* v,
+                           const void* dout, const BwdWork& w, void* dk, void* dv, hipStream_t st) {
   if (p.total == 0 || p.batch == 0) return hipSuccess;
   const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
   const int ntiles = p.batch * nkt * p.hkv;
@@ -580,9 +577,7 @@ hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const
                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), w, dK, dV);
   hipLaunchKernelGGL(bwd128::split_tiles_kernel<true>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,
                      dK, dV);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq(p, q, k, v, dout, w, dq, st);
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -105,10 +105,14 @@ hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* l
                                  const void* dout, const BwdWork& w, bool zero_dkv, hipStream_t st);
 hipError_t launch_bwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
                               const void* dout, const BwdWork& w, void* dq, hipStream_t st);
-// Key-major dK/dV kernel followed by the query-major dQ kernel.
-hipError_t launch_bwd_mfma(const Prefill& p, const void* q, const void* k, const void* v,
-                           const void* dout, const BwdWork& w, void* dq, void* dk, void* dv,
-                           hipStream_t st);
+// Key-major dK/dV pass (planning, the persistent kernel, split-tile finish)
+// and the query-major dQ kernel.  Both read only the inputs and the
+// preprocess's L_new and Delta and write disjoint outputs, so they may run
+// on two streams at once.
+hipError_t launch_bwd_dkdv(const Prefill& p, const void* q, const void* k, const void* v,
+                           const void* dout, const BwdWork& w, void* dk, void* dv, hipStream_t st);
+hipError_t launch_bwd_dq(const Prefill& p, const void* q, const void* k, const void* v,
+                         const void* dout, const BwdWork& w, void* dq, hipStream_t st);
 bool bwd_mfma_supported(const Prefill& p);
 int bwd_num_tiles(const Prefill& p);        // key tiles of the key-major pass
 // Upper bound on the key tiles whose work is split over several work items

@@ -1,12 +1,16 @@
 // C-ABI entry points: host-side validation, workspace carve-up and dispatch
-// to the kernels.  Nothing here reads device memory, allocates, frees or
-// synchronises.
+// to the kernels.  Nothing here reads device memory, allocates device memory,
+// frees or synchronises; the only resources created are the backward's
+// second stream and its two events, once per device.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <utility>
 
 #include "internal.h"
 
@@ -26,6 +30,64 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// The backward's second stream, one per device.  After the preprocess the
+// query-major dQ kernel runs on it while the key-major dK/dV pass runs on the
+// caller's stream: both read only the inputs, L_new and Delta and write
+// disjoint outputs, and the CUs that one kernel's last, unevenly finishing
+// workgroups leave idle take the other's.  The caller's stream forks to it
+// through one event and joins back through another before the call returns,
+// so every output is ordered on the caller's stream as with one stream (under
+// HIP graph capture the fork and the join become graph edges).  Default
+// priority.  Created by the first backward call on a device whose stream is
+// not being captured; before that, if creating it failed, or with
+// SINK_ATTN_SERIAL_BWD=1 in the environment, both passes run on the caller's
+// stream.  One call at a time per device goes through the fork and join (the
+// events are shared); a call made while the side stream belongs to another
+// thread's unfinished capture also runs on one stream.
+struct BwdSide {
+  std::mutex mu;
+  bool tried = false, ok = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+BwdSide g_bwd_side[kMaxSideDevices];
+
+bool serial_bwd_requested() {
+  const char* e = std::getenv("SINK_ATTN_SERIAL_BWD");
+  return e != nullptr && e[0] == '1';
+}
+
+// The current device's side stream, created on first use outside capture,
+// returned with its mutex held in *lock; nullptr when the backward runs on
+// one stream.
+BwdSide* bwd_side(hipStream_t st, std::unique_lock<std::mutex>* lock) {
+  if (serial_bwd_requested()) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long cid = 0;
+  if (hipStreamGetCaptureInfo(st, &cs, &cid) != hipSuccess) return nullptr;
+  BwdSide& side = g_bwd_side[dev];
+  std::unique_lock<std::mutex> held(side.mu);
+  if (!side.tried) {
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
+    side.tried = true;
+    side.ok = hipStreamCreateWithFlags(&side.stream, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&side.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&side.join, hipEventDisableTiming) == hipSuccess;
+  }
+  if (!side.ok) return nullptr;
+  // A side stream that joined a capture stays in it until the capture ends:
+  // use it only from that same capture, else run on one stream.
+  hipStreamCaptureStatus ss = hipStreamCaptureStatusNone;
+  unsigned long long sid = 0;
+  if (hipStreamGetCaptureInfo(side.stream, &ss, &sid) != hipSuccess) return nullptr;
+  if (ss != hipStreamCaptureStatusNone && (cs != hipStreamCaptureStatusActive || sid != cid)) return nullptr;
+  *lock = std::move(held);
+  return &side;
+}
 
 // Longest sample allowed with block lists (the forward's block bitmap).
 constexpr int kMaxBlockSeqlen = 8192 * SINK_ATTN_BLOCK_SIZE;
@@ -477,10 +539,25 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     const bool mfma = sa::bwd_mfma_supported(p);
     hipError_t e;
     if (mfma) {
+      std::unique_lock<std::mutex> lock;
+      BwdSide* side = bwd_side(st, &lock);
       e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dkv=*/false, st);
+      bool forked = false;
+      if (e == hipSuccess && side != nullptr) {
+        e = hipEventRecord(side->fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+        forked = e == hipSuccess;
+      }
+      if (e == hipSuccess) e = sa::launch_bwd_dq(p, q, k, v, dout, w, dq, forked ? side->stream : st);
       if (e == hipSuccess && p.blocks != nullptr) e = sa::launch_block_csr(p, w, st);
-      if (e == hipSuccess) e = sa::launch_bwd_mfma(p, q, k, v, dout, w, dq, dk, dv, st);
+      if (e == hipSuccess) e = sa::launch_bwd_dkdv(p, q, k, v, dout, w, dk, dv, st);
       if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dk, dv, /*dkv_from_acc=*/false, st);
+      if (forked) {
+        // join even after an error, so a capture is never left forked
+        hipError_t j = hipEventRecord(side->join, side->stream);
+        if (j == hipSuccess) j = hipStreamWaitEvent(st, side->join, 0);
+        if (e == hipSuccess) e = j;
+      }
     } else {
       e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dkv=*/true, st);
       if (e == hipSuccess) e = sa::launch_bwd_generic(p, q, k, v, dout, w, dq, st);

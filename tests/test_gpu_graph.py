@@ -1,8 +1,11 @@
-"""Graph capture of the hot path.  The library launches only on the caller's
-stream, allocates and synchronises nothing, and clears its work-queue counters
-and split-tile accumulators with kernels (no memset nodes), so a captured
-forward + backward + decode, replayed several times with eager work and
-synchronisations between the replays, matches the eager results every time."""
+"""Graph capture of the hot path.  The library launches on the caller's stream
+(the backward also on its own second stream, forked from and joined back into
+the caller's through events, which capture turns into graph edges), allocates
+and synchronises nothing, and clears its work-queue counters and split-tile
+accumulators with kernels (no memset nodes), so a captured forward + backward
++ decode, replayed several times with eager work and synchronisations between
+the replays, matches the eager results every time.  The eager step runs
+first, so the backward's second stream exists when the capture starts."""
 import pytest
 import torch
 

@@ -57,6 +57,62 @@ def test_side_stream_bwd():
     assert_dsink(host(dsink), rds, tol)
 
 
+SCHEDULE_CASES = {
+    # whole key tiles only: every output is written in a fixed order
+    "window": dict(lengths=(1500, 700), hq=8, hkv=2, n_sink=4, window=300),
+    # key tiles split over several work items (float32 partials added
+    # atomically) and block lists
+    "blocks_split": dict(lengths=(2600, 130), hq=16, hkv=2, block_lists=dict(n_random=5)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCHEDULE_CASES))
+def test_bwd_two_streams_match_one(name, monkeypatch):
+    """The backward runs dQ on the library's second stream beside dK/dV on the
+    caller's; SINK_ATTN_SERIAL_BWD=1 runs both on the caller's stream.  The
+    kernels are the same, so dQ and dsink (fixed-order writes) are
+    bit-identical, and dK/dV too where no key tile is split; every output also
+    matches the oracle.  Run on a side stream of the caller's, with allocations
+    on the current stream meanwhile."""
+    _announce(f"bwd two streams vs one {name}")
+    c = dict(SCHEDULE_CASES[name])
+    wl = W.make_prefill(name, c.pop("lengths"), c.pop("hq"), c.pop("hkv"), 128, seed=23, **c)
+    q, k, v, cu, bi, sink = prefill_args(wl)
+    do = dev(wl.do, wl.dtype)
+    args = (cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+    o, lse, s = sa.fwd(q, k, v, *args)
+    outs = {}
+    for mode in ("two", "one", "two"):
+        if mode == "one":
+            monkeypatch.setenv("SINK_ATTN_SERIAL_BWD", "1")
+        else:
+            monkeypatch.delenv("SINK_ATTN_SERIAL_BWD", raising=False)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        got = sa.bwd(q, k, v, o, lse, do, *args, stream=side)
+        junk = _churn(16 << 20)
+        torch.cuda.synchronize()
+        del junk
+        outs.setdefault(mode, []).append([t.clone() for t in got])
+    monkeypatch.delenv("SINK_ATTN_SERIAL_BWD", raising=False)
+    one = outs["one"][0]
+    atomic = "split" in name
+    for two in outs["two"]:
+        for nm, a, b in zip(("dq", "dk", "dv", "dsink"), two, one):
+            if atomic and nm in ("dk", "dv"):
+                assert torch.allclose(a.float(), b.float(), rtol=2.0 ** -7, atol=1e-3), nm
+            else:
+                assert torch.equal(a, b), f"{nm} differs between the schedules"
+    kw = oracle_kwargs(wl)
+    rdq, rdk, rdv, rds = oracle.bwd(wl.q.f32, wl.k.f32, wl.v.f32, wl.cu_seqlens, wl.scale, wl.do.f32, **kw)
+    tol = tol_for(wl.dtype)
+    dq, dk, dv, dsink = outs["two"][1]
+    assert_grad(host(dq), rdq, tol, "dQ")
+    assert_grad(host(dk), rdk, tol, "dK")
+    assert_grad(host(dv), rdv, tol, "dV")
+    assert_dsink(host(dsink), rds, tol)
+
+
 def test_side_stream_kvcache_decode():
     _announce("cache decode on a side stream")
     rng = np.random.default_rng(5)
