@@ -554,8 +554,7 @@ int bwd_max_split_tiles(const Prefill& p) {
 
 hipError_t launch_scan(int32_t* off, int n, hipStream_t st);
 
-hipError_t launch_bwd_dkdv(const Prefill& p, const void* q, const void* k, const void* v,
-                           const void* dout, const BwdWork& w, void* dk, void* dv, hipStream_t st) {
+hipError_t launch_bwd_dkdv_plan(const Prefill& p, const BwdWork& w, void* dk, void* dv, hipStream_t st) {
   if (p.total == 0 || p.batch == 0) return hipSuccess;
   const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
   const int ntiles = p.batch * nkt * p.hkv;
@@ -571,6 +570,18 @@ hipError_t launch_bwd_dkdv(const Prefill& p, const void* q, const void* k, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd128::split_tiles_kernel<false>, dim3(ntiles), dim3(256), 0, st, p, w, nkt, nq,
                      dK, dV);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const Prefill& p, const void* q, const void* k, const void* v,
+                           const void* dout, const BwdWork& w, void* dk, void* dv, hipStream_t st) {
+  if (p.total == 0 || p.batch == 0) return hipSuccess;
+  const int nkt = (p.max_seqlen + qm::BN - 1) / qm::BN;
+  const int ntiles = p.batch * nkt * p.hkv;
+  if (ntiles <= 0) return hipSuccess;
+  const int nq = bwd128::num_queues(p);
+  uint16_t* dK = static_cast<uint16_t*>(dk);
+  uint16_t* dV = static_cast<uint16_t*>(dv);
   // Persistent: two 2-wavefront workgroups per CU, a multiple of the queues.
   hipLaunchKernelGGL(bwd128::dkdv_kernel, dim3(512), dim3(128), 0, st, p, nkt, nq,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -105,10 +105,13 @@ hipError_t launch_bwd_preprocess(const Prefill& p, const void* o, const float* l
                                  const void* dout, const BwdWork& w, bool zero_dkv, hipStream_t st);
 hipError_t launch_bwd_generic(const Prefill& p, const void* q, const void* k, const void* v,
                               const void* dout, const BwdWork& w, void* dq, hipStream_t st);
-// Key-major dK/dV pass (planning, the persistent kernel, split-tile finish)
-// and the query-major dQ kernel.  Both read only the inputs and the
-// preprocess's L_new and Delta and write disjoint outputs, so they may run
-// on two streams at once.
+// Key-major dK/dV pass: its planning (chunk plan, split-slot scan, zeroed
+// split accumulators; reads only the inputs and the reverse block lists),
+// then the persistent kernel and the split-tile finish; and the query-major
+// dQ kernel.  dK/dV and dQ read only the inputs and the preprocess's L_new
+// and Delta and write disjoint outputs, so they may run on two streams at
+// once, and the planning beside the preprocess.
+hipError_t launch_bwd_dkdv_plan(const Prefill& p, const BwdWork& w, void* dk, void* dv, hipStream_t st);
 hipError_t launch_bwd_dkdv(const Prefill& p, const void* q, const void* k, const void* v,
                            const void* dout, const BwdWork& w, void* dk, void* dv, hipStream_t st);
 hipError_t launch_bwd_dq(const Prefill& p, const void* q, const void* k, const void* v,

@@ -31,14 +31,17 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// The backward's second stream, one per device.  After the preprocess the
-// query-major dQ kernel runs on it while the key-major dK/dV pass runs on the
-// caller's stream: both read only the inputs, L_new and Delta and write
+// The backward's second stream, one per device.  The caller's stream forks to
+// it at the start of the call; it runs the key-major pass's planning (which
+// reads only the inputs) while the caller's stream runs the preprocess, then
+// waits for the preprocess and runs the query-major dQ kernel while the
+// caller's stream, once the planning is done, runs the key-major dK/dV
+// kernel: dQ and dK/dV read only the inputs, L_new and Delta and write
 // disjoint outputs, and the CUs that one kernel's last, unevenly finishing
-// workgroups leave idle take the other's.  The caller's stream forks to it
-// through one event and joins back through another before the call returns,
-// so every output is ordered on the caller's stream as with one stream (under
-// HIP graph capture the fork and the join become graph edges).  Default
+// workgroups leave idle take the other's.  It joins back into the caller's
+// stream before the call returns, so every output is ordered on the caller's
+// stream as with one stream (under HIP graph capture the events become graph
+// edges).  Default
 // priority.  Created by the first backward call on a device whose stream is
 // not being captured; before that, if creating it failed, or with
 // SINK_ATTN_SERIAL_BWD=1 in the environment, both passes run on the caller's
@@ -49,7 +52,7 @@ struct BwdSide {
   std::mutex mu;
   bool tried = false, ok = false;
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, planned = nullptr, prepped = nullptr, join = nullptr;
 };
 constexpr int kMaxSideDevices = 64;
 BwdSide g_bwd_side[kMaxSideDevices];
@@ -76,6 +79,8 @@ BwdSide* bwd_side(hipStream_t st, std::unique_lock<std::mutex>* lock) {
     side.tried = true;
     side.ok = hipStreamCreateWithFlags(&side.stream, hipStreamNonBlocking) == hipSuccess &&
               hipEventCreateWithFlags(&side.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&side.planned, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&side.prepped, hipEventDisableTiming) == hipSuccess &&
               hipEventCreateWithFlags(&side.join, hipEventDisableTiming) == hipSuccess;
   }
   if (!side.ok) return nullptr;
@@ -541,20 +546,29 @@ int sink_attn_bwd(const sink_attn_prefill_desc* desc, const void* q, const void*
     if (mfma) {
       std::unique_lock<std::mutex> lock;
       BwdSide* side = bwd_side(st, &lock);
-      e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dkv=*/false, st);
+      e = hipSuccess;
       bool forked = false;
-      if (e == hipSuccess && side != nullptr) {
+      if (side != nullptr) {
         e = hipEventRecord(side->fork, st);
         if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
         forked = e == hipSuccess;
       }
-      if (e == hipSuccess) e = sa::launch_bwd_dq(p, q, k, v, dout, w, dq, forked ? side->stream : st);
-      if (e == hipSuccess && p.blocks != nullptr) e = sa::launch_block_csr(p, w, st);
+      hipStream_t ss = forked ? side->stream : st;
+      if (e == hipSuccess && p.blocks != nullptr) e = sa::launch_block_csr(p, w, ss);
+      if (e == hipSuccess) e = sa::launch_bwd_dkdv_plan(p, w, dk, dv, ss);
+      if (e == hipSuccess && forked) e = hipEventRecord(side->planned, ss);
+      if (e == hipSuccess) e = sa::launch_bwd_preprocess(p, o, lse, dout, w, /*zero_dkv=*/false, st);
+      if (e == hipSuccess && forked) {
+        e = hipEventRecord(side->prepped, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(ss, side->prepped, 0);
+      }
+      if (e == hipSuccess) e = sa::launch_bwd_dq(p, q, k, v, dout, w, dq, ss);
+      if (e == hipSuccess && forked) e = hipStreamWaitEvent(st, side->planned, 0);
       if (e == hipSuccess) e = sa::launch_bwd_dkdv(p, q, k, v, dout, w, dk, dv, st);
       if (e == hipSuccess) e = sa::launch_bwd_finish(p, w, dsink, dk, dv, /*dkv_from_acc=*/false, st);
       if (forked) {
         // join even after an error, so a capture is never left forked
-        hipError_t j = hipEventRecord(side->join, side->stream);
+        hipError_t j = hipEventRecord(side->join, ss);
         if (j == hipSuccess) j = hipStreamWaitEvent(st, side->join, 0);
         if (e == hipSuccess) e = j;
       }
