@@ -400,7 +400,10 @@ def head_importance(gate, out=None, stream=None):
 
 def bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen=None, softmax_scale=None, n_sink=0, window=0,
         block_indices=None, learnable_sink=None, stream=None):
-    """Backward.  Returns (dq, dk, dv, dsink float32 [Hq] or None)."""
+    """Backward.  Returns (dq, dk, dv, dsink float32 [Hq] or None).  The
+    library runs part of the work on its own second stream, forked from and
+    joined back into the call's stream inside the call, so the outputs are
+    ordered on the call's stream (SINK_ATTN_SERIAL_BWD=1: one stream)."""
     _need_cuda(q, k, v, o, lse, dout, cu_seqlens, block_indices, learnable_sink)
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
     ms = _max_seqlen(cu_seqlens, max_seqlen)
