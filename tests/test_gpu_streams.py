@@ -113,6 +113,49 @@ def test_bwd_two_streams_match_one(name, monkeypatch):
     assert_dsink(host(dsink), rds, tol)
 
 
+def test_bwd_concurrent_threads():
+    """Two host threads call the backward at once, each on its own stream and
+    with its own inputs (ctypes releases the GIL during the call), so their
+    calls contend for the device's second stream and its events: every result
+    equals the same call made alone (the window case has no split key tiles,
+    so every output is written in a fixed order)."""
+    import threading
+    _announce("bwd from two threads at once")
+    cases = []
+    for i, lengths in enumerate(((1500, 700), (900, 1300, 260))):
+        wl = W.make_prefill(f"thr{i}", list(lengths), 8, 2, 128, n_sink=4, window=300, seed=31 + i)
+        q, k, v, cu, bi, sink = prefill_args(wl)
+        do = dev(wl.do, wl.dtype)
+        args = (cu, wl.max_seqlen, wl.scale, wl.n_sink, wl.window, bi, sink)
+        o, lse, _ = sa.fwd(q, k, v, *args)
+        ref = [t.clone() for t in sa.bwd(q, k, v, o, lse, do, *args)]
+        cases.append((q, k, v, o, lse, do, args, ref))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(c):
+        q, k, v, o, lse, do, args, ref = c
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.default_stream())
+        try:
+            for _ in range(6):
+                got = sa.bwd(q, k, v, o, lse, do, *args, stream=st)
+                st.synchronize()
+                for nm, a, b in zip(("dq", "dk", "dv", "dsink"), got, ref):
+                    if not torch.equal(a, b):
+                        errors.append(f"{nm} differs")
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors[:4]
+
+
 def test_side_stream_kvcache_decode():
     _announce("cache decode on a side stream")
     rng = np.random.default_rng(5)
