@@ -11,7 +11,7 @@
 //
 // Split kernel (bf16, head_dim 128), one workgroup per (sequence b, KV head g,
 // head group, split):
-//   * 4 wavefronts stream disjoint 32-slot chunks of the split.  The query
+//   * 2 wavefronts stream disjoint 32-slot chunks of the split.  The query
 //     heads of the group (up to 16) form the N side of
 //     v_mfma_f32_16x16x32_bf16; S^T = K Q^T puts one head per lane column.
 //   * K goes from HBM straight into the MFMA A-operand registers: lane
@@ -21,7 +21,7 @@
 //   * V is staged through a per-wavefront LDS buffer (rows XOR-swizzled in
 //     16-byte chunks) and read back transposed with ds_read_b64_tr_b16, which
 //     gives each lane one dim at 4 slots: the A operand of O^T += V^T P^T.
-//   * The 4 wavefronts merge (m, l, acc) in LDS; the workgroup writes one
+//   * The wavefronts merge (m, l, acc) in LDS; the workgroup writes one
 //     partial per (b, head, split) to the workspace, or, with a single
 //     split, applies the sink epilogue itself and writes O, LSE and s.
 // Merge kernel (more than one split): M = max_k m_k, l = sum_k e^{m_k - M}
@@ -46,7 +46,13 @@ namespace dec128 {
 
 constexpr int D = 128;
 constexpr int CH = 32;            // slots per chunk
-constexpr int NW = 4;             // wavefronts per workgroup
+// Wavefronts per workgroup.  Two (4 workgroups per CU at 2 wavefronts per
+// SIMD) rather than four: 128 sequences x 8 KV heads then fill the chip in
+// one round of workgroups instead of two, each wavefront streaming twice the
+// chunks (measured, 128 x 4096 slots, Hq 64, Hkv 8: 8-bit cache 0.2245 ->
+// 0.2163 ms, bf16 0.3655 -> 0.3618 ms).
+constexpr int NW = 2;
+constexpr int NT = 64 * NW;       // threads per workgroup
 constexpr int HN = 16;            // query heads per workgroup (N of the MFMA)
 constexpr int VBUF = CH * D;      // bf16 elements of one V chunk buffer (8 KB)
 constexpr float kRescaleLog2 = 8.f;
@@ -105,7 +111,7 @@ __device__ __forceinline__ int kdim(int ks, int gq) {
 }
 
 template <bool Q8>
-__global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
+__global__ __launch_bounds__(NT, 2) void split_kernel(Decode p, int nhg,
                                                        const uint16_t* __restrict__ Q,
                                                        const uint16_t* __restrict__ KC,
                                                        const uint16_t* __restrict__ VC,
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
     ci = cn;
   }
 
-  // Merge the 4 wavefronts.  Per head: m (same on the 4 quarters), l summed
+  // Merge the wavefronts.  Per head: m (same on the 4 quarters), l summed
   // over quarters, acc dims dt*16 + 4gq + i.
   lpart += __shfl_xor(lpart, 16);
   lpart += __shfl_xor(lpart, 32);
@@ -436,10 +442,10 @@ __global__ __launch_bounds__(256, 2) void split_kernel(Decode p, int nhg,
     mbuf[w][l16][D + 1] = lpart;
   }
   __syncthreads();
-  {
-    const int hh = tid >> 4;          // head in group (16)
-    const int d0 = (tid & 15) * 8;    // 8 dims
-    if (hh < nh) {
+  // 16 threads per head, 8 dims each; NT / 16 heads per pass
+  for (int hh = tid >> 4; hh < nh; hh += NT / 16) {
+    const int d0 = (tid & 15) * 8;
+    {
       float M = -kInf;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mbuf[ww][hh][D]);
@@ -541,15 +547,18 @@ bool decode_mfma_supported(const Decode& p) {
 }
 
 int decode_auto_splits(const Decode& p) {
-  // One split (no merge pass) when the (sequence, KV head) units alone give
-  // every CU two workgroups; otherwise enough splits for about 8 per CU, but
-  // no split shorter than 4 chunks per wavefront.  Measured on 128 x 4096
-  // slots, 8 KV heads: 1 split 0.391 ms, 2: 0.410, 4: 0.420, 16: 0.436.
+  // One split (no merge pass) when the (sequence, KV head) units alone fill
+  // every CU's 8 wavefront slots (2 per SIMD) once; otherwise enough splits
+  // for about 4 rounds of workgroups, but no split shorter than 4 chunks per
+  // wavefront.  Measured on 128 x 4096 slots, 8 KV heads (1024 units), with 4
+  // wavefronts per workgroup: 1 split 0.391 ms, 2: 0.410, 4: 0.420, 16:
+  // 0.436; with 2 (the 8-bit cache): 1 split 0.225 ms, 2: 0.248, 4: 0.284.
+  // The thresholds count wavefronts, so they follow NW.
   const int G = p.hq / p.hkv;
   const long long units = static_cast<long long>(p.batch) * p.hkv * ((G + dec128::HN - 1) / dec128::HN);
   if (units <= 0) return 1;
-  if (units >= 512) return 1;
-  long long want = (2048 + units - 1) / units;
+  if (units * dec128::NW >= 2048) return 1;
+  long long want = (8192 / dec128::NW + units - 1) / units;
   const long long max_by_len = p.slots / (dec128::CH * dec128::NW * 4);
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
@@ -563,7 +572,7 @@ hipError_t launch_decode(const Decode& p, const void* q, const void* kc, const v
   const int G = p.hq / p.hkv;
   const int nhg = (G + dec128::HN - 1) / dec128::HN;
   dim3 grid(p.splits, p.hkv * nhg, p.batch);
-  hipLaunchKernelGGL(dec128::split_kernel<false>, grid, dim3(256), 0, st, p, nhg,
+  hipLaunchKernelGGL(dec128::split_kernel<false>, grid, dim3(dec128::NT), 0, st, p, nhg,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), ws, static_cast<uint16_t*>(o), lse, s,
                      KvCache{});
@@ -584,7 +593,7 @@ hipError_t launch_kvcache_decode_q8(const Decode& p, const KvCache& c, const voi
   const int G = p.hq / p.hkv;
   const int nhg = (G + dec128::HN - 1) / dec128::HN;
   dim3 grid(p.splits, p.hkv * nhg, p.batch);
-  hipLaunchKernelGGL(dec128::split_kernel<true>, grid, dim3(256), 0, st, p, nhg,
+  hipLaunchKernelGGL(dec128::split_kernel<true>, grid, dim3(dec128::NT), 0, st, p, nhg,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(c.sink_k),
                      static_cast<const uint16_t*>(c.sink_v), ws, static_cast<uint16_t*>(o), lse, s, c);
   if (p.splits > 1)
