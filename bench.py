@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # reported as null until the counters are taken again.
 FWD_TRAFFIC = {
     "sources": ('fwd_mfma.hip', 'qmajor.cuh', 'common.cuh', 'internal.h', 'stream_rows.cuh'),
-    "sha256": "fa71a6a0686d95338b090d7811f7a90a4aca73faf57284186dad6f39b2d478ba",
-    "read_bytes": 231316048,
-    "write_bytes": 142686052,
+    "sha256": "722fb0cc38f342ca165612e25c9d061aa72f902cf3cd33e6d1d74e3f603e6250",
+    "read_bytes": 231219194,
+    "write_bytes": 142695419,
 }
 
 
